@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Throughput of the ring-attention rank shares on one MI355X.
+
+A step is one pass of the whole forward hot path over one batch of the
+workload: for every simulated rank r of the CP group, ``ra_rank_forward``
+(the diagonal causal block, the C-1 history blocks, the lse merges and the
+bf16 finalisation) on the rank's zig-zag shard, all on one stream.
+
+Default workload: 32K grouped-query causal attention (32 query heads over
+8 KV heads, head dim 128, bf16), zig-zag CP=8, N(0,1)*0.5 inputs.
+
+Prints one JSON line.  ``value`` is the effective attention TFLOP/s of the
+whole step (causal FLOPs counted once: 2*(dqk+dv) per visible pair per
+query head).  ``roofline`` is for the dominant kernel, the bf16 block
+attention forward: algorithmic FLOPs over its average launch duration, the
+durations taken with HIP events the library records on the launch stream
+around every attention launch of the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gqa_32k")
+    ap.add_argument("--fuse-merge", type=int, default=0,
+                    help="1: merge in the attention epilogue instead of ra_lse_merge")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="time budget of the oracle CPU baseline sample (0 = skip)")
+    return ap.parse_args()
+
+
+def kernel_hash() -> str:
+    p = os.path.join(ROOT, "context_blockwise_softmax_ra_amd", "csrc", "attn_fwd_bf16.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def traffic_for(workload: str):
+    """HBM bytes per attention launch from committed counter runs, if still current."""
+    p = os.path.join(ROOT, "profiles", f"traffic_attn_fwd_bf16_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        t = json.load(open(p))
+    except Exception:
+        return None
+    if t.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float):
+    """The fp64 oracle on a bounded sample of rank 0's rows, in effective TFLOP/s."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    cu = w.cu_global()
+    rows, _ = oracle.zigzag_local_tokens(w.cp, 0, cu)
+    rng = np.random.default_rng(0)
+    order = rng.permutation(len(rows))
+    q = synth.cast(w.q(), w.dtype).to(__import__("torch").float64).numpy()
+    k = synth.cast(w.k(), w.dtype).to(__import__("torch").float64).numpy()
+    v = synth.cast(w.v(), w.dtype).to(__import__("torch").float64).numpy()
+    lay = oracle.ref.Layout(cu)
+    done = 0
+    flops = 0.0
+    t0 = time.perf_counter()
+    blk = 32
+    while done < len(rows):
+        sel = rows[order[done:done + blk]]
+        oracle.full_attention(q, k, v, cu, rows=sel)
+        vis = (sel - cu[lay.doc[sel]] + 1).sum()
+        flops += float(vis) * w.hq * 2 * (w.dqk + w.dv)
+        done += len(sel)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"rank 0 of {w.name}: {done} of {len(rows)} local rows (random), all "
+                      f"{w.hq} query heads over every visible key, float64 NumPy, {dt:.1f} s"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only: every simulated rank's "
+                                   "share runs in turn on a single MI355X; run with --gpus 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import synth
+    from context_blockwise_softmax_ra_amd import _lib as L
+    from context_blockwise_softmax_ra_amd.ring import RingProblem
+
+    w = synth.WORKLOADS[a.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"# workload {w.name}: S={w.seqlen} CP={w.cp} hq={w.hq} hkv={w.hkv} "
+          f"d={w.dqk}/{w.dv} {w.dtype}", file=sys.stderr, flush=True)
+    q = synth.cast(w.q(), w.dtype).to(dev)
+    k = synth.cast(w.k(), w.dtype).to(dev)
+    v = synth.cast(w.v(), w.dtype).to(dev)
+    prob = RingProblem(q, k, v, w.cu_global(), w.cp)
+    del q, k, v
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    C = w.cp
+    bufs = [prob.alloc_forward(torch.bfloat16, bool(a.fuse_merge)) for _ in range(C)]
+    work = [prob.work(r) for r in range(C)]                      # per step (pairs*hq, ...)
+    fl_pair = 2 * (w.dqk + w.dv)
+    step_flops = sum(p for r in range(C) for (p, _, _) in work[r]) * fl_pair
+    stream = torch.cuda.current_stream()
+
+    def make_events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record(stream)                                     # create the HIP events
+        return evs
+
+    def run_step(events=None):
+        for r in range(C):
+            out, lse, ws = bufs[r]
+            prob.forward(r, out, lse, ws, fuse_merge=bool(a.fuse_merge),
+                         events=None if events is None else events[r])
+
+    for _ in range(a.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    print("# warmup done", file=sys.stderr, flush=True)
+
+    ev = [[make_events(2 * C) for _ in range(C)] for _ in range(a.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(a.steps):
+        run_step(ev[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / a.steps
+    print(f"# timed {a.steps} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / a.steps:.3f})",
+          file=sys.stderr, flush=True)
+
+    # per-launch attention durations
+    attn_ms = 0.0
+    attn_flops = 0.0
+    diag_ms = hist_ms = 0.0
+    diag_fl = hist_fl = 0.0
+    n_launch = 0
+    for i in range(a.steps):
+        for r in range(C):
+            for s in range(C):
+                d = ev[i][r][2 * s].elapsed_time(ev[i][r][2 * s + 1])
+                f = work[r][s][0] * fl_pair
+                attn_ms += d
+                attn_flops += f
+                n_launch += 1
+                if s == 0:
+                    diag_ms += d
+                    diag_fl += f
+                else:
+                    hist_ms += d
+                    hist_fl += f
+    achieved = attn_flops / (attn_ms / 1e3) / 1e12
+    avg_launch_ms = attn_ms / n_launch
+    value = step_flops / (ms_step / 1e3) / 1e12
+    traffic = traffic_for(w.name)
+
+    res = {
+        "metric": "effective attention TFLOP/s per rank-share (bf16) + % of MFMA peak, 1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)*%g, bf16 RNE)" % w.mult,
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {
+            "workload": f"{w.name}: causal attention, S={w.seqlen}, zig-zag CP={w.cp} "
+                        f"(all {w.cp} rank shares forward, one after another), "
+                        f"{w.hq} q heads / {w.hkv} kv heads, head dim {w.dqk}/{w.dv}",
+            "seq_len": w.seqlen, "cp": w.cp, "hq": w.hq, "hkv": w.hkv, "dqk": w.dqk,
+            "dv": w.dv, "fuse_merge": bool(a.fuse_merge),
+            "step_effective_tflop": round(step_flops / 1e12, 4),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_fwd_bf16",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "avg_launch_ms": round(avg_launch_ms, 5),
+            "launches": n_launch,
+            "diag_tflops": round(diag_fl / (diag_ms / 1e3) / 1e12, 2) if diag_ms else None,
+            "history_tflops": round(hist_fl / (hist_ms / 1e3) / 1e12, 2) if hist_ms else None,
+        },
+        "cpu_baseline": None,
+    }
+    del bufs, prob
+    torch.cuda.empty_cache()
+    if a.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,618 @@
+// Host side of libra.so: argument validation, kernel dispatch, the zig-zag
+// shard map and the per-rank step plan.  No device allocation, no
+// synchronisation; every launch goes on the caller's stream.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "ra_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+ra_status fail(ra_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+ra_status ok() {
+  g_err.clear();
+  return RA_OK;
+}
+
+ra_status hip_fail(hipError_t e, const char* what) {
+  return fail(RA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int part_len(int full, ra_part p) {
+  if (p == RA_PART_ALL) return full;
+  const int half = full >> 1;
+  return p == RA_PART_FIRST_HALF ? half : full - half;
+}
+
+bool bf16_dims_ok(int dqk, int dv) {
+  return (dqk == 128 && dv == 128) || (dqk == 192 && dv == 128) || (dqk == 64 && dv == 64);
+}
+bool f32_dims_ok(int dqk, int dv) {
+  return dqk == dv && (dqk == 16 || dqk == 32 || dqk == 64 || dqk == 128);
+}
+
+// Validates a cu_seqlens host array: non-negative, non-decreasing.
+ra_status check_cu(const int32_t* cu, int n_seq, const char* name) {
+  if (!cu) return fail(RA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (cu[0] < 0) return fail(RA_ERR_INVALID_ARG, "%s[0] < 0", name);
+  for (int s = 0; s < n_seq; ++s)
+    if (cu[s + 1] < cu[s]) return fail(RA_ERR_INVALID_ARG, "%s decreases at %d", name, s);
+  return RA_OK;
+}
+
+struct Checked {
+  int64_t qs, ks, vs;
+  int total_q, total_k;
+  int max_q_part, max_k_part;
+  float scale;
+};
+
+// Full validation of a block descriptor (q/k/v presence controlled by need_kv).
+ra_status check_desc(const ra_attn_desc* d, bool need_kv, Checked* c) {
+  if (!d) return fail(RA_ERR_INVALID_ARG, "descriptor is NULL");
+  if (!d->q) return fail(RA_ERR_INVALID_ARG, "q is NULL");
+  if (need_kv && (!d->k || !d->v)) return fail(RA_ERR_INVALID_ARG, "k or v is NULL");
+  if (d->dtype != RA_BF16 && d->dtype != RA_FP32)
+    return fail(RA_ERR_INVALID_ARG, "unknown dtype %d", (int)d->dtype);
+  if (d->hq <= 0 || d->hkv <= 0) return fail(RA_ERR_INVALID_ARG, "head counts must be > 0");
+  if (d->hq % d->hkv)
+    return fail(RA_ERR_INVALID_ARG, "hq (%d) is not a multiple of hkv (%d)", d->hq, d->hkv);
+  if (d->dqk <= 0 || d->dv <= 0) return fail(RA_ERR_INVALID_ARG, "head dims must be > 0");
+  if (d->dtype == RA_BF16 && !bf16_dims_ok(d->dqk, d->dv))
+    return fail(RA_ERR_UNSUPPORTED, "bf16 (dqk, dv) = (%d, %d) not built", d->dqk, d->dv);
+  if (d->dtype == RA_FP32 && !f32_dims_ok(d->dqk, d->dv))
+    return fail(RA_ERR_UNSUPPORTED, "fp32 (dqk, dv) = (%d, %d) not built", d->dqk, d->dv);
+  if (d->q_part < RA_PART_ALL || d->q_part > RA_PART_SECOND_HALF || d->k_part < RA_PART_ALL ||
+      d->k_part > RA_PART_SECOND_HALF)
+    return fail(RA_ERR_INVALID_ARG, "unknown part selector");
+  if (d->n_seq <= 0) return fail(RA_ERR_INVALID_ARG, "n_seq must be >= 1");
+  if (!d->cu_seqlens_q || !d->cu_seqlens_k)
+    return fail(RA_ERR_INVALID_ARG, "device cu_seqlens is NULL");
+  ra_status st;
+  if ((st = check_cu(d->cu_seqlens_q_host, d->n_seq, "cu_seqlens_q_host")) != RA_OK) return st;
+  if ((st = check_cu(d->cu_seqlens_k_host, d->n_seq, "cu_seqlens_k_host")) != RA_OK) return st;
+  c->qs = d->q_stride_tok ? d->q_stride_tok : (int64_t)d->hq * d->dqk;
+  c->ks = d->k_stride_tok ? d->k_stride_tok : (int64_t)d->hkv * d->dqk;
+  c->vs = d->v_stride_tok ? d->v_stride_tok : (int64_t)d->hkv * d->dv;
+  if (c->qs < (int64_t)d->hq * d->dqk || c->ks < (int64_t)d->hkv * d->dqk ||
+      c->vs < (int64_t)d->hkv * d->dv)
+    return fail(RA_ERR_INVALID_ARG, "token stride smaller than heads * dim");
+  if (d->dtype == RA_BF16) {
+    if (!aligned16(d->q) || (need_kv && (!aligned16(d->k) || !aligned16(d->v))))
+      return fail(RA_ERR_INVALID_ARG, "bf16 q/k/v must be 16-byte aligned");
+    if ((c->qs % 8) || (c->ks % 8) || (c->vs % 8))
+      return fail(RA_ERR_INVALID_ARG, "bf16 token strides must be multiples of 8 elements");
+  }
+  c->total_q = d->cu_seqlens_q_host[d->n_seq];
+  c->total_k = d->cu_seqlens_k_host[d->n_seq];
+  c->max_q_part = 0;
+  c->max_k_part = 0;
+  for (int s = 0; s < d->n_seq; ++s) {
+    const int lq = d->cu_seqlens_q_host[s + 1] - d->cu_seqlens_q_host[s];
+    const int lk = d->cu_seqlens_k_host[s + 1] - d->cu_seqlens_k_host[s];
+    if ((d->q_part != RA_PART_ALL && (lq & 1)) || (d->k_part != RA_PART_ALL && (lk & 1)))
+      return fail(RA_ERR_INVALID_ARG, "segment %d: halves need an even length (q %d, k %d)", s,
+                  lq, lk);
+    const int pq = part_len(lq, d->q_part), pk = part_len(lk, d->k_part);
+    if (d->causal && pq != pk)
+      return fail(RA_ERR_INVALID_ARG,
+                  "segment %d: causal block needs equal q and k part lengths (%d vs %d)", s, pq,
+                  pk);
+    c->max_q_part = std::max(c->max_q_part, pq);
+    c->max_k_part = std::max(c->max_k_part, pk);
+  }
+  c->scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / std::sqrt((float)d->dqk);
+  return RA_OK;
+}
+
+ra::AttnArgs make_args(const ra_attn_desc* d, const Checked& c) {
+  ra::AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = d->q;
+  a.k = d->k;
+  a.v = d->v;
+  a.q_stride = c.qs;
+  a.k_stride = c.ks;
+  a.v_stride = c.vs;
+  a.hq = d->hq;
+  a.hkv = d->hkv;
+  a.group = d->hq / d->hkv;
+  a.n_seq = d->n_seq;
+  a.cu_q = d->cu_seqlens_q;
+  a.cu_k = d->cu_seqlens_k;
+  a.q_part = d->q_part;
+  a.k_part = d->k_part;
+  const int bm = d->dtype == RA_BF16 ? ra::kFwdBlockM : ra::kF32BlockM;
+  a.n_qtiles = (c.max_q_part + bm - 1) / bm;
+  a.n_ktiles = 0;
+  a.scale = c.scale;
+  a.scale_log2 = c.scale * 1.4426950408889634f;
+  a.total_q = c.total_q;
+  return a;
+}
+
+ra_status launch_fwd(const ra_attn_desc* d, const Checked& c, float* out, float* lse, bool merge,
+                     hipStream_t st) {
+  ra::AttnArgs a = make_args(d, c);
+  a.out = out;
+  a.lse = lse;
+  if (a.n_qtiles == 0) return RA_OK;
+  hipError_t e = d->dtype == RA_BF16
+                     ? ra::launch_attn_fwd_bf16(a, d->dqk, d->dv, d->causal != 0, merge, st)
+                     : ra::launch_attn_fwd_f32(a, d->dqk, d->dv, d->causal != 0, merge, st);
+  if (e != hipSuccess) return hip_fail(e, "attention forward launch");
+  return RA_OK;
+}
+
+ra_status check_merge_args(const float* out_acc, const float* lse_acc, const float* out_part,
+                           const float* lse_part, int32_t total_t, int32_t h, int32_t dv,
+                           int32_t n_seq, const int32_t* cu, const int32_t* cu_host,
+                           ra_part rows, int* max_rows) {
+  if (!out_acc || !lse_acc || !out_part || !lse_part || !cu)
+    return fail(RA_ERR_INVALID_ARG, "NULL buffer");
+  if (total_t < 0 || h <= 0 || dv <= 0 || (dv % 4) || dv > 1024)
+    return fail(RA_ERR_INVALID_ARG, "bad sizes (total_t %d, h %d, dv %d)", total_t, h, dv);
+  if (!aligned16(out_acc) || !aligned16(out_part))
+    return fail(RA_ERR_INVALID_ARG, "outputs must be 16-byte aligned");
+  if (rows < RA_PART_ALL || rows > RA_PART_SECOND_HALF)
+    return fail(RA_ERR_INVALID_ARG, "unknown part selector");
+  if (n_seq <= 0) return fail(RA_ERR_INVALID_ARG, "n_seq must be >= 1");
+  ra_status st = check_cu(cu_host, n_seq, "cu_seqlens_host");
+  if (st != RA_OK) return st;
+  if (cu_host[n_seq] > total_t) return fail(RA_ERR_INVALID_ARG, "cu_seqlens beyond total_t");
+  *max_rows = 0;
+  for (int s = 0; s < n_seq; ++s) {
+    const int L = cu_host[s + 1] - cu_host[s];
+    if (rows != RA_PART_ALL && (L & 1))
+      return fail(RA_ERR_INVALID_ARG, "segment %d: halves need an even length", s);
+    *max_rows = std::max(*max_rows, part_len(L, rows));
+  }
+  return RA_OK;
+}
+
+// Step s of rank r: owner j = (r - s) mod C (KV moves 0 -> 1 -> ...).
+struct Step {
+  int owner;
+  int causal;
+  ra_part q_part, k_part;
+};
+
+Step plan_step(int rank, int s, int cp) {
+  Step p;
+  p.owner = ((rank - s) % cp + cp) % cp;
+  if (s == 0) {
+    p.causal = 1;
+    p.q_part = RA_PART_ALL;
+    p.k_part = RA_PART_ALL;
+  } else if (p.owner < rank) {
+    // the owner's first chunk precedes both of ours, its second follows both
+    p.causal = 0;
+    p.q_part = RA_PART_ALL;
+    p.k_part = RA_PART_FIRST_HALF;
+  } else {
+    // both owner chunks lie between our first and our second chunk
+    p.causal = 0;
+    p.q_part = RA_PART_SECOND_HALF;
+    p.k_part = RA_PART_ALL;
+  }
+  return p;
+}
+
+ra_status check_rank_common(const ra_attn_desc& L, int cp, int rank, const void* const* kb,
+                            const void* const* vb, Checked* c) {
+  if (cp <= 0 || rank < 0 || rank >= cp)
+    return fail(RA_ERR_INVALID_ARG, "bad cp_size %d / rank %d", cp, rank);
+  if (!kb || !vb) return fail(RA_ERR_INVALID_ARG, "k_blocks / v_blocks is NULL");
+  for (int j = 0; j < cp; ++j)
+    if (!kb[j] || !vb[j]) return fail(RA_ERR_INVALID_ARG, "KV block of owner %d is NULL", j);
+  if (L.q_part != RA_PART_ALL || L.k_part != RA_PART_ALL)
+    return fail(RA_ERR_INVALID_ARG, "local descriptor parts must be RA_PART_ALL");
+  ra_attn_desc t = L;
+  t.k = kb[0];
+  t.v = vb[0];
+  t.causal = 1;
+  ra_status st = check_desc(&t, true, c);
+  if (st != RA_OK) return st;
+  for (int s = 0; s <= L.n_seq; ++s)
+    if (L.cu_seqlens_q_host[s] != L.cu_seqlens_k_host[s])
+      return fail(RA_ERR_INVALID_ARG, "local q and k cu_seqlens must match");
+  if (cp > 1)
+    for (int s = 0; s < L.n_seq; ++s)
+      if ((L.cu_seqlens_q_host[s + 1] - L.cu_seqlens_q_host[s]) & 1)
+        return fail(RA_ERR_INVALID_ARG, "local segment %d has odd length (zig-zag halves)", s);
+  for (int j = 0; j < cp; ++j)
+    if (L.dtype == RA_BF16 && (!aligned16(kb[j]) || !aligned16(vb[j])))
+      return fail(RA_ERR_INVALID_ARG, "KV block %d not 16-byte aligned", j);
+  return RA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+const char* ra_last_error(void) { return g_err.c_str(); }
+
+const char* ra_version(void) { return "0.1.0"; }
+
+ra_status ra_block_attn_fwd(const ra_attn_desc* d, float* out, float* lse, void* stream) {
+  Checked c;
+  ra_status st = check_desc(d, true, &c);
+  if (st != RA_OK) return st;
+  if (!out || !lse) return fail(RA_ERR_INVALID_ARG, "out or lse is NULL");
+  if (!aligned16(out)) return fail(RA_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  st = launch_fwd(d, c, out, lse, false, (hipStream_t)stream);
+  return st == RA_OK ? ok() : st;
+}
+
+ra_status ra_block_attn_fwd_merge(const ra_attn_desc* d, float* out_acc, float* lse_acc,
+                                  void* stream) {
+  Checked c;
+  ra_status st = check_desc(d, true, &c);
+  if (st != RA_OK) return st;
+  if (!out_acc || !lse_acc) return fail(RA_ERR_INVALID_ARG, "out_acc or lse_acc is NULL");
+  if (!aligned16(out_acc)) return fail(RA_ERR_INVALID_ARG, "out_acc must be 16-byte aligned");
+  st = launch_fwd(d, c, out_acc, lse_acc, true, (hipStream_t)stream);
+  return st == RA_OK ? ok() : st;
+}
+
+ra_status ra_lse_merge(float* out_acc, float* lse_acc, const float* out_part,
+                       const float* lse_part, int32_t total_t, int32_t h, int32_t dv,
+                       int32_t n_seq, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                       ra_part rows, void* stream) {
+  int max_rows = 0;
+  ra_status st = check_merge_args(out_acc, lse_acc, out_part, lse_part, total_t, h, dv, n_seq,
+                                  cu_seqlens, cu_seqlens_host, rows, &max_rows);
+  if (st != RA_OK) return st;
+  hipError_t e = ra::launch_lse_merge(out_acc, lse_acc, out_part, lse_part, total_t, h, dv,
+                                      n_seq, cu_seqlens, rows, max_rows, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "lse merge launch");
+  return ok();
+}
+
+ra_status ra_zigzag_shard_map(int32_t cp_size, int32_t rank, int32_t n_seq,
+                              const int32_t* cu_seqlens_global, int32_t* cu_seqlens_local,
+                              int32_t* src_start) {
+  if (cp_size <= 0 || rank < 0 || rank >= cp_size)
+    return fail(RA_ERR_INVALID_ARG, "bad cp_size %d / rank %d", cp_size, rank);
+  if (n_seq <= 0) return fail(RA_ERR_INVALID_ARG, "n_seq must be >= 1");
+  if (!cu_seqlens_local || !src_start) return fail(RA_ERR_INVALID_ARG, "NULL output");
+  ra_status st = check_cu(cu_seqlens_global, n_seq, "cu_seqlens_global");
+  if (st != RA_OK) return st;
+  const int two_c = 2 * cp_size;
+  for (int s = 0; s < n_seq; ++s) {
+    const int L = cu_seqlens_global[s + 1] - cu_seqlens_global[s];
+    if (L % two_c)
+      return fail(RA_ERR_INVALID_ARG, "sequence %d length %d is not a multiple of 2*cp_size %d",
+                  s, L, two_c);
+  }
+  cu_seqlens_local[0] = 0;
+  for (int s = 0; s < n_seq; ++s) {
+    const int g0 = cu_seqlens_global[s];
+    const int c = (cu_seqlens_global[s + 1] - g0) / two_c;
+    src_start[2 * s] = g0 + rank * c;
+    src_start[2 * s + 1] = g0 + (two_c - 1 - rank) * c;
+    cu_seqlens_local[s + 1] = cu_seqlens_local[s] + 2 * c;
+  }
+  return ok();
+}
+
+static ra_status zigzag_copy(const void* src, void* dst, int64_t row_bytes, int32_t n_seq,
+                             const int32_t* cu_local, const int32_t* start,
+                             const int32_t* cu_local_host, const int32_t* start_host,
+                             int32_t total_global, bool gather, hipStream_t st) {
+  if (!src || !dst || !cu_local || !start || !cu_local_host || !start_host)
+    return fail(RA_ERR_INVALID_ARG, "NULL argument");
+  if (row_bytes <= 0 || (row_bytes % 16) || !aligned16(src) || !aligned16(dst))
+    return fail(RA_ERR_INVALID_ARG, "rows must be 16-byte multiples and aligned");
+  if (n_seq <= 0) return fail(RA_ERR_INVALID_ARG, "n_seq must be >= 1");
+  ra_status s = check_cu(cu_local_host, n_seq, "cu_seqlens_local_host");
+  if (s != RA_OK) return s;
+  int max_half = 0;
+  for (int i = 0; i < n_seq; ++i) {
+    const int L = cu_local_host[i + 1] - cu_local_host[i];
+    if (L & 1) return fail(RA_ERR_INVALID_ARG, "local segment %d has odd length", i);
+    const int c = L / 2;
+    for (int j = 0; j < 2; ++j)
+      if (start_host[2 * i + j] < 0 || (int64_t)start_host[2 * i + j] + c > total_global)
+        return fail(RA_ERR_INVALID_ARG, "segment %d half %d outside the global buffer", i, j);
+    max_half = std::max(max_half, c);
+  }
+  hipError_t e = ra::launch_zigzag_copy(src, dst, row_bytes, n_seq, cu_local, start, max_half,
+                                        gather, st);
+  if (e != hipSuccess) return hip_fail(e, "zig-zag copy launch");
+  return ok();
+}
+
+ra_status ra_zigzag_gather(const void* global_src, void* local_dst, int64_t row_bytes,
+                           int32_t n_seq, const int32_t* cu_seqlens_local,
+                           const int32_t* src_start, const int32_t* cu_seqlens_local_host,
+                           const int32_t* src_start_host, int32_t total_global, void* stream) {
+  return zigzag_copy(global_src, local_dst, row_bytes, n_seq, cu_seqlens_local, src_start,
+                     cu_seqlens_local_host, src_start_host, total_global, true,
+                     (hipStream_t)stream);
+}
+
+ra_status ra_zigzag_scatter(const void* local_src, void* global_dst, int64_t row_bytes,
+                            int32_t n_seq, const int32_t* cu_seqlens_local,
+                            const int32_t* src_start, const int32_t* cu_seqlens_local_host,
+                            const int32_t* src_start_host, int32_t total_global, void* stream) {
+  return zigzag_copy(local_src, global_dst, row_bytes, n_seq, cu_seqlens_local, src_start,
+                     cu_seqlens_local_host, src_start_host, total_global, false,
+                     (hipStream_t)stream);
+}
+
+ra_status ra_cast_f32_bf16(const float* src, void* dst, int64_t n, void* stream) {
+  if (!src || !dst) return fail(RA_ERR_INVALID_ARG, "NULL buffer");
+  if (n < 0 || (n % 4)) return fail(RA_ERR_INVALID_ARG, "n must be a multiple of 4");
+  if (!aligned16(src) || (reinterpret_cast<uintptr_t>(dst) & 7u))
+    return fail(RA_ERR_INVALID_ARG, "misaligned buffers");
+  hipError_t e = ra::launch_cast_f32_bf16(src, dst, n, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "cast launch");
+  return ok();
+}
+
+ra_status ra_rank_forward_workspace(const ra_rank_desc* d, size_t* bytes) {
+  if (!d || !bytes) return fail(RA_ERR_INVALID_ARG, "NULL argument");
+  Checked c;
+  ra_status st = check_rank_common(d->local, d->cp_size, d->rank, d->k_blocks, d->v_blocks, &c);
+  if (st != RA_OK) return st;
+  const size_t out_b = align256((size_t)c.total_q * d->local.hq * d->local.dv * sizeof(float));
+  const size_t lse_b = align256((size_t)c.total_q * d->local.hq * sizeof(float));
+  size_t b = 0;
+  if (d->out_dtype != RA_FP32) b += out_b;                   // fp32 accumulator
+  if (!d->fuse_merge && d->cp_size > 1) b += out_b + lse_b;  // one partial
+  *bytes = b;
+  return ok();
+}
+
+ra_status ra_rank_forward(const ra_rank_desc* d, void* stream) {
+  if (!d) return fail(RA_ERR_INVALID_ARG, "descriptor is NULL");
+  hipStream_t hs = (hipStream_t)stream;
+  Checked c;
+  ra_status st = check_rank_common(d->local, d->cp_size, d->rank, d->k_blocks, d->v_blocks, &c);
+  if (st != RA_OK) return st;
+  if (!d->out || !d->lse) return fail(RA_ERR_INVALID_ARG, "out or lse is NULL");
+  if (d->out_dtype != RA_BF16 && d->out_dtype != RA_FP32)
+    return fail(RA_ERR_INVALID_ARG, "unknown out_dtype");
+  if (!aligned16(d->out)) return fail(RA_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  size_t need = 0;
+  if ((st = ra_rank_forward_workspace(d, &need)) != RA_OK) return st;
+  if (need && (!d->workspace || d->workspace_bytes < need))
+    return fail(RA_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", d->workspace_bytes,
+                need);
+  if (need && !aligned16(d->workspace))
+    return fail(RA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const ra_attn_desc& L = d->local;
+  const size_t out_b = align256((size_t)c.total_q * L.hq * L.dv * sizeof(float));
+  char* ws = static_cast<char*>(d->workspace);
+  float* acc = nullptr;
+  if (d->out_dtype == RA_FP32) {
+    acc = static_cast<float*>(d->out);
+  } else {
+    acc = reinterpret_cast<float*>(ws);
+    ws += out_b;
+  }
+  float* part_out = nullptr;
+  float* part_lse = nullptr;
+  if (!d->fuse_merge && d->cp_size > 1) {
+    part_out = reinterpret_cast<float*>(ws);
+    ws += out_b;
+    part_lse = reinterpret_cast<float*>(ws);
+  }
+  hipError_t e;
+  for (int s = 0; s < d->cp_size; ++s) {
+    const Step p = plan_step(d->rank, s, d->cp_size);
+    ra_attn_desc sd = L;
+    sd.k = d->k_blocks[p.owner];
+    sd.v = d->v_blocks[p.owner];
+    sd.causal = p.causal;
+    sd.q_part = p.q_part;
+    sd.k_part = p.k_part;
+    Checked cs;
+    if ((st = check_desc(&sd, true, &cs)) != RA_OK) return st;
+    if (d->events && d->events[2 * s] &&
+        (e = hipEventRecord((hipEvent_t)d->events[2 * s], hs)) != hipSuccess)
+      return hip_fail(e, "event record");
+    if (s == 0) {
+      st = launch_fwd(&sd, cs, acc, d->lse, false, hs);  // the diagonal starts the result
+    } else if (d->fuse_merge) {
+      st = launch_fwd(&sd, cs, acc, d->lse, true, hs);
+    } else {
+      st = launch_fwd(&sd, cs, part_out, part_lse, false, hs);
+    }
+    if (st != RA_OK) return st;
+    if (d->events && d->events[2 * s + 1] &&
+        (e = hipEventRecord((hipEvent_t)d->events[2 * s + 1], hs)) != hipSuccess)
+      return hip_fail(e, "event record");
+    if (s > 0 && !d->fuse_merge) {
+      e = ra::launch_lse_merge(acc, d->lse, part_out, part_lse, c.total_q, L.hq, L.dv, L.n_seq,
+                               L.cu_seqlens_q, p.q_part, cs.max_q_part, hs);
+      if (e != hipSuccess) return hip_fail(e, "lse merge launch");
+    }
+  }
+  if (d->out_dtype == RA_BF16) {
+    e = ra::launch_cast_f32_bf16(acc, d->out, (int64_t)c.total_q * L.hq * L.dv, hs);
+    if (e != hipSuccess) return hip_fail(e, "cast launch");
+  }
+  return ok();
+}
+
+ra_status ra_attn_bwd_delta(const void* out, ra_dtype out_dtype, const void* dout,
+                            ra_dtype dout_dtype, int32_t total_t, int32_t hq, int32_t dv,
+                            float* delta, void* stream) {
+  if (!out || !dout || !delta) return fail(RA_ERR_INVALID_ARG, "NULL buffer");
+  if ((out_dtype != RA_BF16 && out_dtype != RA_FP32) ||
+      (dout_dtype != RA_BF16 && dout_dtype != RA_FP32))
+    return fail(RA_ERR_INVALID_ARG, "unknown dtype");
+  if (total_t < 0 || hq <= 0 || dv <= 0) return fail(RA_ERR_INVALID_ARG, "bad sizes");
+  hipError_t e = ra::launch_bwd_delta(out, out_dtype, dout, dout_dtype, total_t, hq, dv, delta,
+                                      (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "delta launch");
+  return ok();
+}
+
+static ra_status launch_bwd(const ra_attn_desc* d, const Checked& c, const void* dout,
+                            const float* lse, const float* delta, float* dq, float* dk, float* dv,
+                            hipStream_t st) {
+  ra::AttnArgs a = make_args(d, c);
+  a.dout = dout;
+  a.lse_in = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  hipError_t e = ra::launch_attn_bwd_bf16(a, d->dqk, d->dv, d->causal != 0, st);
+  if (e == hipErrorInvalidValue) return fail(RA_ERR_UNSUPPORTED, "backward variant not built");
+  if (e != hipSuccess) return hip_fail(e, "attention backward launch");
+  return RA_OK;
+}
+
+static ra_status check_bwd_extra(const ra_attn_desc* d, const void* dout, const float* lse,
+                                 const float* delta, const float* dq, const float* dk,
+                                 const float* dv) {
+  if (!dout || !lse || !delta || !dq || !dk || !dv)
+    return fail(RA_ERR_INVALID_ARG, "NULL buffer");
+  if (d->dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "backward is bf16 only");
+  if (!((d->dqk == 128 && d->dv == 128) || (d->dqk == 192 && d->dv == 128)))
+    return fail(RA_ERR_UNSUPPORTED, "backward (dqk, dv) = (%d, %d) not built", d->dqk, d->dv);
+  if (d->q_stride_tok && d->q_stride_tok != (int64_t)d->hq * d->dqk)
+    return fail(RA_ERR_UNSUPPORTED, "backward needs packed q (dq shares its layout)");
+  if (d->k_stride_tok && d->k_stride_tok != (int64_t)d->hkv * d->dqk)
+    return fail(RA_ERR_UNSUPPORTED, "backward needs packed k");
+  if (d->v_stride_tok && d->v_stride_tok != (int64_t)d->hkv * d->dv)
+    return fail(RA_ERR_UNSUPPORTED, "backward needs packed v");
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(RA_ERR_INVALID_ARG, "backward buffers must be 16-byte aligned");
+  return RA_OK;
+}
+
+ra_status ra_block_attn_bwd(const ra_attn_desc* d, const void* dout, const float* lse,
+                            const float* delta, float* dq_acc, float* dk_acc, float* dv_acc,
+                            void* stream) {
+  Checked c;
+  ra_status st = check_desc(d, true, &c);
+  if (st != RA_OK) return st;
+  if ((st = check_bwd_extra(d, dout, lse, delta, dq_acc, dk_acc, dv_acc)) != RA_OK) return st;
+  st = launch_bwd(d, c, dout, lse, delta, dq_acc, dk_acc, dv_acc, (hipStream_t)stream);
+  return st == RA_OK ? ok() : st;
+}
+
+ra_status ra_rank_backward_workspace(const ra_rank_bwd_desc* d, size_t* bytes) {
+  if (!d || !bytes) return fail(RA_ERR_INVALID_ARG, "NULL argument");
+  Checked c;
+  ra_status st = check_rank_common(d->local, d->cp_size, d->rank, d->k_blocks, d->v_blocks, &c);
+  if (st != RA_OK) return st;
+  *bytes = align256((size_t)c.total_q * d->local.hq * sizeof(float));
+  return ok();
+}
+
+ra_status ra_rank_backward(const ra_rank_bwd_desc* d, void* stream) {
+  if (!d) return fail(RA_ERR_INVALID_ARG, "descriptor is NULL");
+  hipStream_t hs = (hipStream_t)stream;
+  Checked c;
+  ra_status st = check_rank_common(d->local, d->cp_size, d->rank, d->k_blocks, d->v_blocks, &c);
+  if (st != RA_OK) return st;
+  if (!d->out || !d->dout || !d->lse || !d->dq || !d->dk_blocks || !d->dv_blocks)
+    return fail(RA_ERR_INVALID_ARG, "NULL buffer");
+  if (d->out_dtype != RA_BF16 && d->out_dtype != RA_FP32)
+    return fail(RA_ERR_INVALID_ARG, "unknown out_dtype");
+  for (int j = 0; j < d->cp_size; ++j)
+    if (!d->dk_blocks[j] || !d->dv_blocks[j])
+      return fail(RA_ERR_INVALID_ARG, "gradient block of owner %d is NULL", j);
+  size_t need = 0;
+  if ((st = ra_rank_backward_workspace(d, &need)) != RA_OK) return st;
+  if (!d->workspace || d->workspace_bytes < need)
+    return fail(RA_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", d->workspace_bytes,
+                need);
+  const ra_attn_desc& L = d->local;
+  for (int j = 0; j < d->cp_size; ++j) {
+    ra_attn_desc t = L;
+    t.k = d->k_blocks[j];
+    t.v = d->v_blocks[j];
+    if ((st = check_bwd_extra(&t, d->dout, d->lse, static_cast<const float*>(d->workspace),
+                              d->dq, d->dk_blocks[j], d->dv_blocks[j])) != RA_OK)
+      return st;
+  }
+  float* delta = static_cast<float*>(d->workspace);
+  hipError_t e = ra::launch_bwd_delta(d->out, d->out_dtype, d->dout, L.dtype, c.total_q, L.hq,
+                                      L.dv, delta, hs);
+  if (e != hipSuccess) return hip_fail(e, "delta launch");
+  for (int s = 0; s < d->cp_size; ++s) {
+    const Step p = plan_step(d->rank, s, d->cp_size);
+    ra_attn_desc sd = L;
+    sd.k = d->k_blocks[p.owner];
+    sd.v = d->v_blocks[p.owner];
+    sd.causal = p.causal;
+    sd.q_part = p.q_part;
+    sd.k_part = p.k_part;
+    Checked cs;
+    if ((st = check_desc(&sd, true, &cs)) != RA_OK) return st;
+    if (d->events && d->events[2 * s] &&
+        (e = hipEventRecord((hipEvent_t)d->events[2 * s], hs)) != hipSuccess)
+      return hip_fail(e, "event record");
+    st = launch_bwd(&sd, cs, d->dout, d->lse, delta, d->dq, d->dk_blocks[p.owner],
+                    d->dv_blocks[p.owner], hs);
+    if (st != RA_OK) return st;
+    if (d->events && d->events[2 * s + 1] &&
+        (e = hipEventRecord((hipEvent_t)d->events[2 * s + 1], hs)) != hipSuccess)
+      return hip_fail(e, "event record");
+  }
+  return ok();
+}
+
+ra_status ra_block_attn_work(const ra_attn_desc* d, int64_t* visible_pairs,
+                             int64_t* tiles_visited, int64_t* tiles_skipped) {
+  Checked c;
+  ra_status st = check_desc(d, false, &c);
+  if (st != RA_OK) return st;
+  if (!visible_pairs || !tiles_visited || !tiles_skipped)
+    return fail(RA_ERR_INVALID_ARG, "NULL output");
+  const int bm = d->dtype == RA_BF16 ? ra::kFwdBlockM : ra::kF32BlockM;
+  const int bn = d->dtype == RA_BF16 ? ra::kFwdBlockN : ra::kF32BlockN;
+  int64_t pairs = 0, vis = 0, skip = 0;
+  for (int s = 0; s < d->n_seq; ++s) {
+    const int lq = part_len(d->cu_seqlens_q_host[s + 1] - d->cu_seqlens_q_host[s], d->q_part);
+    const int lk = part_len(d->cu_seqlens_k_host[s + 1] - d->cu_seqlens_k_host[s], d->k_part);
+    if (d->causal)
+      for (int i = 0; i < lq; ++i) pairs += std::min(lk, i + 1);
+    else
+      pairs += (int64_t)lq * lk;
+    const int all_tiles = (lk + bn - 1) / bn;
+    for (int q0 = 0; q0 < lq; q0 += bm) {
+      const int last = std::min(q0 + bm, lq) - 1;
+      const int kend = d->causal ? std::min(lk, last + 1) : lk;
+      const int v = (kend + bn - 1) / bn;
+      vis += v;
+      skip += all_tiles - v;
+    }
+  }
+  *visible_pairs = pairs * d->hq;
+  *tiles_visited = vis * d->hq;
+  *tiles_skipped = skip * d->hq;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,219 @@
+// Bandwidth-bound kernels of the rank share: the lse merge, the float32 ->
+// bfloat16 finalisation, the zig-zag gather/scatter and the backward's
+// row dot product delta = rowsum(dout * out).
+//
+// All of them stream [tokens, heads, dim] rows with 16-byte accesses; a
+// group of consecutive lanes covers one (token, head) row, so every wave
+// instruction touches whole, contiguous rows.
+
+#include "ra_internal.h"
+
+namespace ra {
+namespace {
+
+constexpr int NT = 256;
+
+__device__ __forceinline__ int pow2ceil_le64(int x) {
+  int p = 1;
+  while (p < x && p < 64) p <<= 1;
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// lse merge ("超长序列并行训练技术：Ulysses与Ring-Attention详解", section 4.2:
+// lse_new = log(exp(lse_prev) + exp(lse_cur)); the output is re-weighted by
+// exp(lse_side - lse_new), the exact correction of the oh-bug page's
+// online softmax).  Each (token, head) row is handled by one lane group that
+// reads both lse values before any lane writes the new one; a group never
+// spans two waves, so the read-before-write order holds without barriers.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NT) void lse_merge_kernel(float* __restrict__ out_acc,
+                                                       float* __restrict__ lse_acc,
+                                                       const float* __restrict__ out_part,
+                                                       const float* __restrict__ lse_part,
+                                                       int total_t, int h, int dv,
+                                                       const int* __restrict__ cu, int part) {
+  const int seg = blockIdx.y;
+  int lo, hi;
+  part_range(cu[seg], cu[seg + 1], part, &lo, &hi);
+  const int nrows = (hi - lo) * h;
+  const int c4n = dv >> 2;
+  const int lg = pow2ceil_le64(c4n);
+  const int per_wave = 64 / lg;
+  const int lane = threadIdx.x & 63;
+  const int sub = lane / lg, li = lane % lg;
+  const int wave_global = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
+  const int wstride = gridDim.x * (NT / 64);
+  for (int base = wave_global * per_wave; base < nrows; base += wstride * per_wave) {
+    const int rh = base + sub;
+    const bool ok = rh < nrows;
+    const int t = lo + (ok ? rh / h : 0);
+    const int hh = ok ? rh % h : 0;
+    float la = -INFINITY, lb = -INFINITY;
+    if (ok) {
+      la = lse_acc[(int64_t)hh * total_t + t];
+      lb = lse_part[(int64_t)hh * total_t + t];
+    }
+    const float m = fmaxf(la, lb);
+    const bool empty = (m == -INFINITY);
+    const float ms = empty ? 0.f : m;
+    const float wa = __expf(la - ms), wb = __expf(lb - ms);
+    const float tot = wa + wb;
+    const float ca = empty ? 0.f : wa / tot;
+    const float cb = empty ? 0.f : wb / tot;
+    if (ok) {
+      float4* pa = reinterpret_cast<float4*>(out_acc + ((int64_t)t * h + hh) * dv);
+      const float4* pb = reinterpret_cast<const float4*>(out_part + ((int64_t)t * h + hh) * dv);
+      for (int c = li; c < c4n; c += lg) {
+        const float4 x = pa[c], y = pb[c];
+        float4 r;
+        r.x = ca * x.x + cb * y.x;
+        r.y = ca * x.y + cb * y.y;
+        r.z = ca * x.z + cb * y.z;
+        r.w = ca * x.w + cb * y.w;
+        pa[c] = r;
+      }
+    }
+    // every lane of the wave has read both lse values by now
+    if (ok && li == 0) lse_acc[(int64_t)hh * total_t + t] = empty ? -INFINITY : ms + __logf(tot);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// float32 -> bfloat16, round to nearest even (NaN kept quiet)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
+  unsigned u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (unsigned short)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+
+__global__ __launch_bounds__(NT) void cast_kernel(const float4* __restrict__ src,
+                                                  ushort4* __restrict__ dst, int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n4; i += (int64_t)gridDim.x * NT) {
+    const float4 x = src[i];
+    ushort4 y;
+    y.x = f32_to_bf16_rne(x.x);
+    y.y = f32_to_bf16_rne(x.y);
+    y.z = f32_to_bf16_rne(x.z);
+    y.w = f32_to_bf16_rne(x.w);
+    dst[i] = y;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// zig-zag gather / scatter: local half 2d+j of segment d starts at global
+// token src_start[2d+j] ("超长序列并行训练技术", section 4.2 placement).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NT) void zigzag_copy_kernel(const uint4* __restrict__ src,
+                                                         uint4* __restrict__ dst,
+                                                         int64_t row16, const int* __restrict__ cu,
+                                                         const int* __restrict__ start,
+                                                         int gather) {
+  const int seg = blockIdx.y;
+  const int l0 = cu[seg], l1 = cu[seg + 1];
+  const int c = (l1 - l0) >> 1;
+  const int64_t n = (int64_t)(l1 - l0) * row16;
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) {
+    const int r = (int)(i / row16);
+    const int64_t w = i % row16;
+    const int half = r >= c ? 1 : 0;
+    const int64_t g = (int64_t)start[2 * seg + half] + (r - half * c);
+    const int64_t loc = (int64_t)(l0 + r);
+    if (gather)
+      dst[loc * row16 + w] = src[g * row16 + w];
+    else
+      dst[g * row16 + w] = src[loc * row16 + w];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// delta[h, t] = sum_d dout[t, h, d] * out[t, h, d]
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float ld_elem(const void* p, int dtype, int64_t i) {
+  if (dtype == RA_FP32) return reinterpret_cast<const float*>(p)[i];
+  const unsigned short b = reinterpret_cast<const unsigned short*>(p)[i];
+  return __uint_as_float((unsigned)b << 16);
+}
+
+__global__ __launch_bounds__(NT) void bwd_delta_kernel(const void* __restrict__ out, int odt,
+                                                       const void* __restrict__ dout, int ddt,
+                                                       int total_t, int h, int dv,
+                                                       float* __restrict__ delta) {
+  // one (token, head) row per 16-lane group, 4 groups per wave
+  const int lane = threadIdx.x & 63;
+  const int sub = lane >> 4, li = lane & 15;
+  const int64_t nrows = (int64_t)total_t * h;
+  const int64_t wave_global = (int64_t)blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
+  const int64_t wstride = (int64_t)gridDim.x * (NT / 64);
+  for (int64_t base = wave_global * 4; base < nrows; base += wstride * 4) {
+    const int64_t rh = base + sub;
+    float acc = 0.f;
+    if (rh < nrows) {
+      const int64_t off = rh * dv;
+      for (int d = li; d < dv; d += 16) acc += ld_elem(out, odt, off + d) * ld_elem(dout, ddt, off + d);
+    }
+#pragma unroll
+    for (int s = 8; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 16);
+    if (rh < nrows && li == 0) {
+      const int64_t t = rh / h, hh = rh % h;
+      delta[hh * total_t + t] = acc;
+    }
+  }
+}
+
+unsigned grid_for(int64_t work, int64_t per_block, unsigned cap) {
+  int64_t g = (work + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return (unsigned)g;
+}
+
+}  // namespace
+
+hipError_t launch_lse_merge(float* out_acc, float* lse_acc, const float* out_part,
+                            const float* lse_part, int32_t total_t, int32_t h, int32_t dv,
+                            int32_t n_seq, const int32_t* cu, int32_t part, int32_t max_rows,
+                            hipStream_t st) {
+  if (n_seq <= 0 || max_rows <= 0) return hipSuccess;
+  int c4n = dv / 4, lg = 1;
+  while (lg < c4n && lg < 64) lg <<= 1;
+  const int rows_per_block = (NT / lg);
+  dim3 grid(grid_for((int64_t)max_rows * h, rows_per_block, 65535u), (unsigned)n_seq);
+  hipLaunchKernelGGL(lse_merge_kernel, grid, dim3(NT), 0, st, out_acc, lse_acc, out_part,
+                     lse_part, total_t, h, dv, cu, part);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_f32_bf16(const float* src, void* dst, int64_t n, hipStream_t st) {
+  const int64_t n4 = n / 4;
+  if (n4 <= 0) return hipSuccess;
+  hipLaunchKernelGGL(cast_kernel, dim3(grid_for(n4, NT, 8192u)), dim3(NT), 0, st,
+                     reinterpret_cast<const float4*>(src), reinterpret_cast<ushort4*>(dst), n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_zigzag_copy(const void* src, void* dst, int64_t row_bytes, int32_t n_seq,
+                              const int32_t* cu_local, const int32_t* src_start,
+                              int32_t max_half, bool gather, hipStream_t st) {
+  if (n_seq <= 0 || max_half <= 0) return hipSuccess;
+  const int64_t row16 = row_bytes / 16;
+  dim3 grid(grid_for((int64_t)2 * max_half * row16, NT, 4096u), (unsigned)n_seq);
+  hipLaunchKernelGGL(zigzag_copy_kernel, grid, dim3(NT), 0, st,
+                     reinterpret_cast<const uint4*>(src), reinterpret_cast<uint4*>(dst), row16,
+                     cu_local, src_start, gather ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_delta(const void* out, int out_dtype, const void* dout, int dout_dtype,
+                            int32_t total_t, int32_t hq, int32_t dv, float* delta,
+                            hipStream_t st) {
+  const int64_t rows = (int64_t)total_t * hq;
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_delta_kernel, dim3(grid_for(rows, 16, 16384u)), dim3(NT), 0, st, out,
+                     out_dtype, dout, dout_dtype, total_t, hq, dv, delta);
+  return hipGetLastError();
+}
+
+}  // namespace ra

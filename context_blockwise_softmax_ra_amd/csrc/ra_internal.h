@@ -1,0 +1,85 @@
+// Internal declarations shared by the host API and the HIP kernels of libra.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ra.h"
+
+namespace ra {
+
+// Geometry of the bf16 MFMA forward kernel: 4 waves x 32 query rows per
+// workgroup, key tiles of 64.
+constexpr int kFwdWaves = 4;
+constexpr int kFwdRowsPerWave = 32;
+constexpr int kFwdBlockM = kFwdWaves * kFwdRowsPerWave;  // 128
+constexpr int kFwdBlockN = 64;
+
+// fp32 forward kernel: one query row per lane, one wave per workgroup.
+constexpr int kF32BlockM = 64;
+constexpr int kF32BlockN = 32;
+
+// Arguments of every attention kernel (forward and backward).
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t q_stride, k_stride, v_stride;  // elements between tokens
+  int32_t hq, hkv, group;                // group = hq / hkv
+  int32_t n_seq;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int32_t q_part, k_part;
+  int32_t n_qtiles;       // query tiles per segment (max over segments)
+  int32_t n_ktiles;       // key tiles per segment (max over segments; backward)
+  float scale;            // softmax scale
+  float scale_log2;       // scale * log2(e)
+  int32_t total_q;        // lse / delta row stride
+  // forward outputs (fp32): out [total_q, hq, dv], lse [hq, total_q]
+  float* out;
+  float* lse;
+  // backward
+  const void* dout;       // [total_q, hq, dv], same dtype as q
+  const float* lse_in;    // final lse [hq, total_q]
+  const float* delta;     // [hq, total_q]
+  float* dq;              // [total_q, hq, dqk] fp32 accumulate
+  float* dk;              // [total_k, hkv, dqk] fp32 accumulate
+  float* dv;              // [total_k, hkv, dv] fp32 accumulate
+};
+
+// Segment part [lo, hi) after applying a zig-zag half selector.
+__host__ __device__ inline void part_range(int32_t s0, int32_t s1, int32_t part, int32_t* lo,
+                                           int32_t* hi) {
+  int32_t half = (s1 - s0) >> 1;
+  if (part == RA_PART_FIRST_HALF) {
+    *lo = s0;
+    *hi = s0 + half;
+  } else if (part == RA_PART_SECOND_HALF) {
+    *lo = s0 + half;
+    *hi = s1;
+  } else {
+    *lo = s0;
+    *hi = s1;
+  }
+}
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int dqk, int dv, bool causal, bool merge,
+                                hipStream_t st);
+hipError_t launch_attn_fwd_f32(const AttnArgs& a, int dqk, int dv, bool causal, bool merge,
+                               hipStream_t st);
+hipError_t launch_lse_merge(float* out_acc, float* lse_acc, const float* out_part,
+                            const float* lse_part, int32_t total_t, int32_t h, int32_t dv,
+                            int32_t n_seq, const int32_t* cu, int32_t part, int32_t max_rows,
+                            hipStream_t st);
+hipError_t launch_cast_f32_bf16(const float* src, void* dst, int64_t n, hipStream_t st);
+hipError_t launch_zigzag_copy(const void* src, void* dst, int64_t row_bytes, int32_t n_seq,
+                              const int32_t* cu_local, const int32_t* src_start,
+                              int32_t max_half, bool gather, hipStream_t st);
+hipError_t launch_bwd_delta(const void* out, int out_dtype, const void* dout, int dout_dtype,
+                            int32_t total_t, int32_t hq, int32_t dv, float* delta,
+                            hipStream_t st);
+hipError_t launch_attn_bwd_bf16(const AttnArgs& a, int dqk, int dv, bool causal,
+                                hipStream_t st);
+
+}  // namespace ra

@@ -1,0 +1,272 @@
+/*
+ * ra.h -- C ABI of libra.so: one context-parallel rank's share of Ring
+ * Attention on an AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages cited by title and section):
+ *   - "超长序列并行训练技术：Ulysses与Ring-Attention详解" (intelliparadigm):
+ *     section 4.1 -- attention is computed block by block, each block
+ *     returning a partial output and its log-sum-exp (lse), folded into a
+ *     running result; section 4.2 -- partials merge by
+ *     lse_new = log(exp(lse_prev) + exp(lse_cur)), and the sequence is
+ *     placed zig-zag: device i holds chunk i and chunk 2C-1-i; section 4.3
+ *     -- the backward recomputes forward quantities instead of storing them;
+ *     section 5.3 -- each sequence is padded on its own to a multiple of
+ *     2 x world size.
+ *   - "LLM Context Parallel production guide" (oh-bug): local Q is kept,
+ *     KV blocks travel the ring, each step's attention is merged exactly by
+ *     per-row max and exp-sum; packed varlen metadata (cumulative lengths)
+ *     follows the same sequence mapping; kernels should skip dead causal
+ *     blocks.
+ *   - "超长上下文训练速度翻倍秘籍" (ant-ling), section 2, "踩坑一": the
+ *     diagonal block (local Q x local KV) is causal; received history KV
+ *     blocks are fully visible and use a non-causal call.
+ *
+ * Conventions for every entry point:
+ *   - Layout: token-major packed tensors [tokens, heads, dim] with dim
+ *     contiguous; lse and delta are [heads, tokens] float32.
+ *   - Packed sequences: segment s covers tokens [cu[s], cu[s+1]) of a
+ *     buffer.  Both a host and a device copy of every cu_seqlens array are
+ *     passed: the host copy is used for validation and launch sizing only
+ *     (it is not retained), the device copy by the kernels.
+ *   - Ownership: the caller allocates and frees every buffer, including
+ *     workspaces; the library keeps no pointer after a call returns, keeps
+ *     no state except a thread-local error string, never synchronises and
+ *     never allocates device memory.  Work is queued on the caller's stream
+ *     (a hipStream_t passed as void*; NULL = the null stream); buffers must
+ *     outlive the queued work.
+ *   - Errors: arguments are validated before anything is queued; on
+ *     RA_ERR_INVALID_ARG / RA_ERR_UNSUPPORTED nothing is launched and
+ *     nothing is written.  A failed launch returns RA_ERR_HIP.  Faults of
+ *     queued work surface at the caller's next synchronisation.
+ *     ra_last_error() describes the last non-OK status of the thread.
+ */
+#ifndef RA_H
+#define RA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RA_OK = 0,
+  RA_ERR_INVALID_ARG = 1,
+  RA_ERR_UNSUPPORTED = 2,
+  RA_ERR_HIP = 3
+} ra_status;
+
+typedef enum { RA_BF16 = 0, RA_FP32 = 1 } ra_dtype;
+
+/* Which half of every segment takes part in a block (zig-zag halves). */
+typedef enum {
+  RA_PART_ALL = 0,
+  RA_PART_FIRST_HALF = 1,  /* tokens [cu[s], cu[s] + len/2)   */
+  RA_PART_SECOND_HALF = 2  /* tokens [cu[s] + len/2, cu[s+1]) */
+} ra_part;
+
+/*
+ * One block of attention: local queries against one KV block.
+ *
+ * q [total_q, hq, dqk], k [total_k, hkv, dqk], v [total_k, hkv, dv], all of
+ * `dtype`, device memory, token stride q_stride_tok / k_stride_tok /
+ * v_stride_tok elements (>= heads*dim; 0 means packed).  Query head h reads
+ * kv head h / (hq / hkv) (hq % hkv == 0).  Segment s of q and of k are
+ * matched one to one; within a segment only the part selected by q_part /
+ * k_part takes part (segment lengths must then be even).  causal = 1 masks
+ * key j of the part against query i of the part unless j <= i (both counted
+ * from the part's start); it requires equal q and k part lengths in every
+ * segment.  causal = 0 makes every key of the segment part visible.
+ * softmax_scale <= 0 selects 1/sqrt(dqk).
+ *
+ * Supported: bf16 with (dqk, dv) in {(64,64), (128,128), (192,128)};
+ * fp32 with dqk, dv <= 128 and multiples of 4.
+ */
+typedef struct ra_attn_desc {
+  const void* q;
+  const void* k;
+  const void* v;
+  ra_dtype dtype;
+  int32_t hq, hkv, dqk, dv;
+  int64_t q_stride_tok, k_stride_tok, v_stride_tok;
+  int32_t n_seq;
+  const int32_t* cu_seqlens_q;       /* device int32[n_seq + 1] */
+  const int32_t* cu_seqlens_k;       /* device int32[n_seq + 1] */
+  const int32_t* cu_seqlens_q_host;  /* host   int32[n_seq + 1] */
+  const int32_t* cu_seqlens_k_host;  /* host   int32[n_seq + 1] */
+  ra_part q_part, k_part;
+  int32_t causal;
+  float softmax_scale;
+} ra_attn_desc;
+
+/*
+ * Partial attention of one block (intelliparadigm section 4.1: a block
+ * returns (out, lse)).  out [total_q, hq, dv] float32 and lse [hq, total_q]
+ * float32 (natural log) are written for the covered query rows only
+ * (rows outside q_part keep their contents).  A covered row that sees no
+ * key gets out = 0, lse = -inf.
+ */
+ra_status ra_block_attn_fwd(const ra_attn_desc* d, float* out, float* lse, void* stream);
+
+/*
+ * Same block, merged straight into a running result instead of written as
+ * a partial: for the covered rows, (out_acc, lse_acc) <- merge(acc, block)
+ * with the lse rule of ra_lse_merge.  Saves the partial's round trip
+ * through memory (the oh-bug page's exact online-softmax merge, done in
+ * the attention kernel's epilogue).
+ */
+ra_status ra_block_attn_fwd_merge(const ra_attn_desc* d, float* out_acc, float* lse_acc,
+                                  void* stream);
+
+/*
+ * Merge a partial into a running result, for the covered rows of every
+ * segment (intelliparadigm section 4.2 and the oh-bug page's exact merge):
+ *   lse = m + log(exp(lse_acc - m) + exp(lse_part - m)),  m = max of the two
+ *   out = exp(lse_acc - lse) out_acc + exp(lse_part - lse) out_part
+ * (0, -inf) on either side is the identity; both -inf give (0, -inf).
+ * out_* [total_t, h, dv] float32, lse_* [h, total_t] float32, device.
+ * dv must be a multiple of 4.
+ */
+ra_status ra_lse_merge(float* out_acc, float* lse_acc, const float* out_part,
+                       const float* lse_part, int32_t total_t, int32_t h, int32_t dv,
+                       int32_t n_seq, const int32_t* cu_seqlens,
+                       const int32_t* cu_seqlens_host, ra_part rows, void* stream);
+
+/*
+ * Zig-zag shard map (intelliparadigm section 4.2; per-sequence splitting
+ * as in its section 5.3 and the oh-bug page's varlen rule).  Host only.
+ * Every sequence d of the global packed stream (length L, L % (2*cp_size)
+ * == 0) is cut into 2*cp_size chunks of c = L / (2*cp_size) tokens; `rank`
+ * holds chunk rank and chunk 2*cp_size-1-rank of every sequence, in that
+ * order.  Writes cu_seqlens_local[n_seq+1] (= global / cp_size) and
+ * src_start[2*n_seq]: the global token where local half 2d / 2d+1 starts.
+ */
+ra_status ra_zigzag_shard_map(int32_t cp_size, int32_t rank, int32_t n_seq,
+                              const int32_t* cu_seqlens_global, int32_t* cu_seqlens_local,
+                              int32_t* src_start);
+
+/*
+ * Copy a rank's rows out of a global packed buffer (gather) or back into it
+ * (scatter), using the map above.  Rows are row_bytes long (a multiple of
+ * 16); src_start and cu_seqlens_local are device copies of the map, host
+ * copies are used for validation.  total_global bounds the global buffer.
+ */
+ra_status ra_zigzag_gather(const void* global_src, void* local_dst, int64_t row_bytes,
+                           int32_t n_seq, const int32_t* cu_seqlens_local,
+                           const int32_t* src_start, const int32_t* cu_seqlens_local_host,
+                           const int32_t* src_start_host, int32_t total_global, void* stream);
+ra_status ra_zigzag_scatter(const void* local_src, void* global_dst, int64_t row_bytes,
+                            int32_t n_seq, const int32_t* cu_seqlens_local,
+                            const int32_t* src_start, const int32_t* cu_seqlens_local_host,
+                            const int32_t* src_start_host, int32_t total_global, void* stream);
+
+/*
+ * float32 -> bfloat16, round to nearest even (n elements, multiple of 4).
+ */
+ra_status ra_cast_f32_bf16(const float* src, void* dst, int64_t n, void* stream);
+
+/*
+ * One rank's whole forward share (the ring loop of the oh-bug page: local
+ * Q against every KV block in turn, merged exactly).  `local` describes the
+ * rank's local Q (k, v ignored) and the local cu_seqlens, which are the
+ * same for the rank's own KV block and every received one.  At step s the
+ * block of owner j = (rank - s) mod cp_size is used (KV moves rank 0 -> 1
+ * -> ... as in the iqiancheng page, section 1.1):
+ *   s = 0      : causal, all local rows x all keys (the diagonal block);
+ *   j < rank   : non-causal, all rows x FIRST half of the owner's keys;
+ *   j > rank   : non-causal, SECOND half of the rows x all the owner's keys
+ * (derived from the global causal rule and the zig-zag placement; the
+ * other quarter of each history block is entirely masked and is skipped).
+ * k_blocks / v_blocks: host arrays [cp_size] of device pointers, by owner.
+ * out [total_q, hq, dv] of out_dtype, lse [hq, total_q] float32: final.
+ * fuse_merge = 0: each step writes a partial to the workspace and
+ * ra_lse_merge folds it; 1: steps merge in the attention epilogue.
+ * events (optional): host array of 2*cp_size hipEvent_t, recorded on the
+ * stream right before / after step s's attention launch.
+ */
+typedef struct ra_rank_desc {
+  ra_attn_desc local;
+  int32_t cp_size, rank;
+  const void* const* k_blocks;
+  const void* const* v_blocks;
+  void* out;
+  ra_dtype out_dtype;
+  float* lse;
+  void* workspace;
+  size_t workspace_bytes;
+  int32_t fuse_merge;
+  void* const* events;
+} ra_rank_desc;
+
+ra_status ra_rank_forward_workspace(const ra_rank_desc* d, size_t* bytes);
+ra_status ra_rank_forward(const ra_rank_desc* d, void* stream);
+
+/*
+ * Backward, recomputing the probabilities from the saved final lse
+ * (intelliparadigm section 4.3):
+ *   delta_i = dout_i . out_i                      (ra_attn_bwd_delta)
+ *   P_ij = exp(scale q_i.k_j - lse_i), dV_j += sum_i P_ij dout_i,
+ *   dS_ij = P_ij (dout_i . v_j - delta_i),
+ *   dQ_i += scale sum_j dS_ij k_j,  dK_j += scale sum_i dS_ij q_i
+ * over the block's visible pairs (ra_block_attn_bwd).  dq_acc
+ * [total_q, hq, dqk], dk_acc [total_k, hkv, dqk], dv_acc [total_k, hkv, dv]
+ * are float32 accumulators that are ADDED to (the caller zeroes them);
+ * query heads of a group add into their kv head.  dout has the desc's
+ * dtype; lse and delta are [hq, total_q] float32.  bf16 only, with
+ * (dqk, dv) in {(128,128), (192,128)}.  Deterministic: no atomics.
+ */
+ra_status ra_attn_bwd_delta(const void* out, ra_dtype out_dtype, const void* dout,
+                            ra_dtype dout_dtype, int32_t total_t, int32_t hq, int32_t dv,
+                            float* delta, void* stream);
+ra_status ra_block_attn_bwd(const ra_attn_desc* d, const void* dout, const float* lse,
+                            const float* delta, float* dq_acc, float* dk_acc, float* dv_acc,
+                            void* stream);
+
+/*
+ * One rank's whole backward share: the same step plan as ra_rank_forward;
+ * dK/dV of step s are added into dk_blocks[j] / dv_blocks[j] of the owner
+ * j (in a real ring they travel back to it).  out is the final forward
+ * output (out_dtype), lse the final lse; delta is computed into the
+ * workspace.  dq [total_q, hq, dqk] float32 is added to.
+ */
+typedef struct ra_rank_bwd_desc {
+  ra_attn_desc local;
+  int32_t cp_size, rank;
+  const void* const* k_blocks;
+  const void* const* v_blocks;
+  const void* out;
+  ra_dtype out_dtype;
+  const void* dout;
+  const float* lse;
+  float* dq;
+  float* const* dk_blocks;
+  float* const* dv_blocks;
+  void* workspace;
+  size_t workspace_bytes;
+  void* const* events;
+} ra_rank_bwd_desc;
+
+ra_status ra_rank_backward_workspace(const ra_rank_bwd_desc* d, size_t* bytes);
+ra_status ra_rank_backward(const ra_rank_bwd_desc* d, void* stream);
+
+/*
+ * Accounting (the oh-bug page asks to monitor effective attention blocks
+ * per rank): for one block descriptor, the number of (query, key) pairs
+ * that are visible, the key tiles the forward kernel visits, and the key
+ * tiles it skips as entirely masked, summed over query heads.  Host only.
+ */
+ra_status ra_block_attn_work(const ra_attn_desc* d, int64_t* visible_pairs,
+                             int64_t* tiles_visited, int64_t* tiles_skipped);
+
+/* Thread-local description of the last non-OK status ("" if none). */
+const char* ra_last_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* ra_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA_H */

@@ -1,0 +1,229 @@
+"""CPU checks of the C ABI: exports, host-side logic and argument validation.
+
+No test here launches a kernel: invalid descriptors are rejected before
+anything is queued, and the shard map / accounting entry points are host
+only.  Fake (never dereferenced) device pointers stand in where a pointer
+must be non-NULL.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+R = pytest.importorskip("context_blockwise_softmax_ra_amd")
+from context_blockwise_softmax_ra_amd import _lib as L  # noqa: E402
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "ra.h")
+FAKE = 0x100000  # 16-byte aligned, never dereferenced
+
+
+def declared_symbols():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.lib()
+    syms = declared_symbols()
+    assert len(syms) >= 16
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert sorted(L.EXPORTS) == syms
+
+
+def test_version_and_empty_error():
+    assert L.ra_version() == "0.1.0"
+
+
+# ---------------------------------------------------------------------------
+# zig-zag shard map
+# ---------------------------------------------------------------------------
+
+def test_shard_map_matches_printed_cp4_example():
+    rows = [tuple(int(x) for x in ln.split()) for ln in open(
+        os.path.join(os.path.dirname(__file__), "golden", "zigzag_cp4.txt"))
+        if ln.strip() and not ln.startswith("#")]
+    for C, r, a, b in rows:
+        cl, ss = L.ra_zigzag_shard_map(C, r, [0, 8 * 2 * C])
+        assert list(cl) == [0, 16]
+        assert list(ss) == [8 * a, 8 * b]
+
+
+@pytest.mark.parametrize("lengths,C", [([256], 2), ([8192], 4), ([64, 32, 96, 128], 4),
+                                       ([32] * 5, 16)])
+def test_shard_map_matches_oracle(lengths, C):
+    cu = synth.cu_seqlens(lengths)
+    for r in range(C):
+        cl, ss = L.ra_zigzag_shard_map(C, r, cu)
+        idx, cl_o = oracle.zigzag_local_tokens(C, r, cu)
+        assert np.array_equal(cl, cl_o)
+        got = np.concatenate([np.arange(ss[2 * s + h], ss[2 * s + h] + (cl[s + 1] - cl[s]) // 2)
+                              for s in range(len(cl) - 1) for h in (0, 1)])
+        assert np.array_equal(got, idx)
+
+
+def test_shard_map_varlen_workload_balance():
+    w = synth.WORKLOADS["varlen_128k"]
+    cu = w.cu_global()
+    cls = [L.ra_zigzag_shard_map(w.cp, r, cu)[0] for r in range(w.cp)]
+    for cl in cls:
+        assert np.array_equal(cl, cls[0])
+        assert np.array_equal(cl, cu // w.cp)
+
+
+def test_shard_map_rejects_bad_input():
+    with pytest.raises(L.RaError) as e:
+        L.ra_zigzag_shard_map(4, 0, [0, 12])
+    assert e.value.status == L.RA_ERR_INVALID_ARG
+    assert "multiple of 2*cp_size" in str(e.value)
+    with pytest.raises(L.RaError):
+        L.ra_zigzag_shard_map(4, 4, [0, 16])
+    with pytest.raises(L.RaError):
+        L.ra_zigzag_shard_map(2, 0, [0, 8, 4])
+
+
+# ---------------------------------------------------------------------------
+# descriptor validation (nothing launched)
+# ---------------------------------------------------------------------------
+
+def _desc(T=256, hq=8, hkv=8, dqk=128, dv=128, dtype=L.RA_BF16, cu=None, q_part=0, k_part=0,
+          causal=0):
+    cu = np.array([0, T], dtype=np.int32) if cu is None else np.asarray(cu, np.int32)
+    d = L.AttnDesc()
+    d.q = d.k = d.v = FAKE
+    d.dtype = dtype
+    d.hq, d.hkv, d.dqk, d.dv = hq, hkv, dqk, dv
+    d.q_stride_tok = d.k_stride_tok = d.v_stride_tok = 0
+    d.n_seq = len(cu) - 1
+    d.cu_seqlens_q = d.cu_seqlens_k = FAKE
+    d.cu_seqlens_q_host = d.cu_seqlens_k_host = cu.ctypes.data
+    d.q_part, d.k_part, d.causal = q_part, k_part, causal
+    d.softmax_scale = 0.0
+    d._keep = cu
+    return d
+
+
+def _status(d):
+    return L.lib().ra_block_attn_fwd(ctypes.byref(d), FAKE, FAKE, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(hq=8, hkv=3), L.RA_ERR_INVALID_ARG, "multiple of hkv"),
+    (dict(dqk=96, dv=96), L.RA_ERR_UNSUPPORTED, "not built"),
+    (dict(dtype=L.RA_FP32, dqk=192, dv=128), L.RA_ERR_UNSUPPORTED, "not built"),
+    (dict(cu=[0, 7], q_part=1), L.RA_ERR_INVALID_ARG, "even length"),
+    (dict(cu=[0, 8], q_part=1, causal=1), L.RA_ERR_INVALID_ARG, "equal q and k part"),
+    (dict(cu=[0, 8, 4]), L.RA_ERR_INVALID_ARG, "decreases"),
+    (dict(hq=0), L.RA_ERR_INVALID_ARG, "> 0"),
+    (dict(dtype=7), L.RA_ERR_INVALID_ARG, "dtype"),
+])
+def test_invalid_descriptors_are_rejected_before_launch(kw, status, msg):
+    d = _desc(**kw)
+    assert _status(d) == status
+    assert msg in L.ra_last_error()
+
+
+def test_null_pointers_rejected():
+    d = _desc()
+    d.q = None
+    assert _status(d) == L.RA_ERR_INVALID_ARG
+    assert L.lib().ra_block_attn_fwd(None, FAKE, FAKE, None) == L.RA_ERR_INVALID_ARG
+    d = _desc()
+    assert L.lib().ra_block_attn_fwd(ctypes.byref(d), None, FAKE, None) == L.RA_ERR_INVALID_ARG
+    d.q = FAKE + 2  # misaligned bf16
+    assert _status(d) == L.RA_ERR_INVALID_ARG and "aligned" in L.ra_last_error()
+
+
+def test_merge_and_cast_validation():
+    lib = L.lib()
+    cu = np.array([0, 7], dtype=np.int32)
+    assert lib.ra_lse_merge(FAKE, FAKE, FAKE, FAKE, 7, 2, 128, 1, FAKE, cu.ctypes.data, 2,
+                            None) == L.RA_ERR_INVALID_ARG          # odd length halves
+    assert lib.ra_lse_merge(FAKE, FAKE, FAKE, FAKE, 7, 2, 130, 1, FAKE, cu.ctypes.data, 0,
+                            None) == L.RA_ERR_INVALID_ARG          # dv % 4
+    assert lib.ra_cast_f32_bf16(FAKE, FAKE, 6, None) == L.RA_ERR_INVALID_ARG
+
+
+def test_backward_validation():
+    lib = L.lib()
+    d = _desc(dtype=L.RA_FP32, dqk=64, dv=64)
+    assert lib.ra_block_attn_bwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 None) == L.RA_ERR_UNSUPPORTED
+    d = _desc(dqk=64, dv=64)
+    assert lib.ra_block_attn_bwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 None) == L.RA_ERR_UNSUPPORTED
+
+
+def test_rank_forward_validation():
+    cu = np.array([0, 7], dtype=np.int32)    # odd local length: no zig-zag halves
+    local = _desc(cu=cu)
+    blocks = [FAKE] * 2
+    rd = L.RankDesc()
+    rd.local = local
+    rd.cp_size, rd.rank = 2, 0
+    kb = (ctypes.c_void_p * 2)(*blocks)
+    rd.k_blocks = rd.v_blocks = ctypes.cast(kb, ctypes.c_void_p)
+    rd.out = rd.lse = FAKE
+    rd.out_dtype = L.RA_BF16
+    n = ctypes.c_size_t(0)
+    assert L.lib().ra_rank_forward_workspace(ctypes.byref(rd), ctypes.byref(n)) == L.RA_ERR_INVALID_ARG
+    assert "odd length" in L.ra_last_error()
+    rd.rank = 2
+    assert L.lib().ra_rank_forward(ctypes.byref(rd), None) == L.RA_ERR_INVALID_ARG
+
+
+def test_rank_forward_workspace_sizes():
+    cu = np.array([0, 256], dtype=np.int32)
+    local = _desc(cu=cu, hq=4, hkv=2)
+    kb = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    rd = L.RankDesc()
+    rd.local = local
+    rd.cp_size, rd.rank = 2, 1
+    rd.k_blocks = rd.v_blocks = ctypes.cast(kb, ctypes.c_void_p)
+    rd.out = rd.lse = FAKE
+    rd.out_dtype = L.RA_BF16
+    n = ctypes.c_size_t(0)
+    assert L.lib().ra_rank_forward_workspace(ctypes.byref(rd), ctypes.byref(n)) == 0
+    assert n.value == 2 * 256 * 4 * 128 * 4 + 256 * 4 * 4
+    rd.fuse_merge = 1
+    assert L.lib().ra_rank_forward_workspace(ctypes.byref(rd), ctypes.byref(n)) == 0
+    assert n.value == 256 * 4 * 128 * 4
+
+
+# ---------------------------------------------------------------------------
+# accounting vs the oracle's pair counts
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("lengths,C,hq", [([256], 2, 1), ([8192], 4, 8), ([64, 192, 32, 224], 4, 2)])
+def test_work_accounting_matches_oracle_pairs(lengths, C, hq):
+    cu = synth.cu_seqlens(lengths)
+    for r in range(C):
+        cl, _ = L.ra_zigzag_shard_map(C, r, cu)
+        tot = 0
+        for s in range(C):
+            j = oracle.ring_owner(r, s, C)
+            if s == 0:
+                parts = (0, 0, 1)
+            elif j < r:
+                parts = (0, 1, 0)
+            else:
+                parts = (2, 0, 0)
+            d = _desc(cu=cl, hq=hq, hkv=1, q_part=parts[0], k_part=parts[1], causal=parts[2])
+            pairs, vis, skip = L.ra_block_attn_work(d)
+            rm, km, _ = oracle.step_coverage(cu, C, r, s)
+            # per-step pairs: rows x keys of the step that the global rule allows
+            lay = oracle.ref.Layout(cu)
+            rows, _ = oracle.zigzag_local_tokens(C, r, cu)
+            krows, _ = oracle.zigzag_local_tokens(C, j, cu)
+            vis_m = oracle.ref._visible(lay.pos[rows], lay.doc[rows], lay.pos[krows],
+                                        lay.doc[krows], True)
+            assert pairs == hq * int(vis_m.sum())
+            tot += pairs
+            assert vis >= 0 and skip >= 0
+        assert tot == hq * oracle.visible_pairs(cu, C, r)

@@ -1,0 +1,334 @@
+"""GPU parity of the forward path against the fp64 oracle, through the C ABI.
+
+Covers every forward row of the hot path: the zig-zag gather/scatter, the
+block attention kernels (bf16 MFMA and fp32), the lse merge, the bf16
+finalisation, and whole rank shares for the five workloads (in full where
+the oracle finishes in seconds, else reduced sizes in full plus sampled
+rows at full size).
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import (check_lse, check_out, global_inputs, log, make_problem, metrics,
+                      sample_rows, to_np)
+
+pytestmark = pytest.mark.gpu
+
+R = pytest.importorskip("context_blockwise_softmax_ra_amd")
+from context_blockwise_softmax_ra_amd import _lib as L  # noqa: E402
+
+DEV = torch.device("cuda:0")
+
+
+# ---------------------------------------------------------------------------
+# oracle for one block descriptor (segments, halves, causal within parts)
+# ---------------------------------------------------------------------------
+
+def _part(a, b, part):
+    h = (b - a) // 2
+    return (a, a + h) if part == 1 else ((a + h, b) if part == 2 else (a, b))
+
+
+def block_ref(q, k, v, cu_q, cu_k, q_part, k_part, causal, scale=None):
+    """out [Tq, hq, dv] (0 outside covered rows), lse [hq, Tq] (nan outside), covered mask."""
+    Tq, hq, _ = q.shape
+    dv = v.shape[2]
+    out = np.zeros((Tq, hq, dv))
+    lse = np.full((hq, Tq), np.nan)
+    cov = np.zeros(Tq, bool)
+    for s in range(len(cu_q) - 1):
+        q0, q1 = _part(cu_q[s], cu_q[s + 1], q_part)
+        k0, k1 = _part(cu_k[s], cu_k[s + 1], k_part)
+        if q1 <= q0:
+            continue
+        qp = np.arange(q1 - q0)
+        kp = np.arange(k1 - k0)
+        o, l = oracle.attention(q[q0:q1], k[k0:k1], v[k0:k1], qp, np.zeros_like(qp), kp,
+                                np.zeros_like(kp), scale=scale, causal=causal)
+        out[q0:q1], lse[:, q0:q1], cov[q0:q1] = o, l, True
+    return out, lse, cov
+
+
+def run_block(q, k, v, cu_q, cu_k, q_part, k_part, causal, merge_into=None):
+    dq = q.to(DEV)
+    dk = k.to(DEV)
+    dvv = v.to(DEV)
+    cuq = torch.from_numpy(np.asarray(cu_q, np.int32)).to(DEV)
+    cuk = torch.from_numpy(np.asarray(cu_k, np.int32)).to(DEV)
+    desc = L.attn_desc(dq, dk, dvv, cuq, cuk, cu_q, cu_k, q_part=q_part, k_part=k_part,
+                       causal=causal)
+    Tq, hq = q.shape[0], q.shape[1]
+    if merge_into is None:
+        out = torch.full((Tq, hq, v.shape[2]), 7.0, dtype=torch.float32, device=DEV)
+        lse = torch.full((hq, Tq), 7.0, dtype=torch.float32, device=DEV)
+        L.ra_block_attn_fwd(desc, out, lse)
+    else:
+        out, lse = (t.clone().to(DEV) for t in merge_into)
+        L.ra_block_attn_fwd_merge(desc, out, lse)
+    torch.cuda.synchronize()
+    return to_np(out), to_np(lse)
+
+
+EDGE_CASES = [
+    # name, segment q lengths, segment k lengths, q_part, k_part, causal, hq, hkv
+    ("ragged_causal", [333], [333], 0, 0, True, 4, 2),
+    ("multi_seg_noncausal", [5, 0, 130, 64, 1], [9, 3, 200, 1, 64], 0, 0, False, 2, 2),
+    ("causal_multi_seg_tiny", [1, 2, 129, 64, 63], [1, 2, 129, 64, 63], 0, 0, True, 2, 1),
+    ("halves_q2_kall", [2, 300, 130, 0], [2, 300, 130, 0], 2, 0, False, 4, 4),
+    ("halves_qall_k1", [2, 300, 130, 256], [2, 300, 130, 256], 0, 1, False, 4, 1),
+    ("causal_halves", [260, 4], [260, 4], 1, 1, True, 2, 2),
+    ("empty_keys", [64, 70], [0, 5], 0, 0, False, 2, 2),
+]
+
+
+def _cu(lengths):
+    return synth.cu_seqlens(lengths)
+
+
+@pytest.mark.parametrize("dims", [(128, 128), (192, 128), (64, 64)])
+@pytest.mark.parametrize("case", EDGE_CASES, ids=[c[0] for c in EDGE_CASES])
+def test_block_fwd_bf16_edge_cases(case, dims):
+    name, lq, lk, qp, kp, causal, hq, hkv = case
+    dqk, dv = dims
+    log(f"case {name} dims {dims}")
+    cu_q, cu_k = _cu(lq), _cu(lk)
+    g = torch.Generator().manual_seed(zlib.crc32(f"{name}{dims}".encode()) & 0xFFFF)
+    q = torch.randn(int(cu_q[-1]), hq, dqk, generator=g).to(torch.bfloat16)
+    k = torch.randn(int(cu_k[-1]), hkv, dqk, generator=g).to(torch.bfloat16)
+    v = torch.randn(int(cu_k[-1]), hkv, dv, generator=g).to(torch.bfloat16)
+    out, lse = run_block(q, k, v, cu_q, cu_k, qp, kp, causal)
+    ro, rl, cov = block_ref(to_np(q), to_np(k), to_np(v), cu_q, cu_k, qp, kp, causal)
+    check_out(out[cov], ro[cov], "bf16", name)
+    check_lse(lse[:, cov], rl[:, cov], name)
+    # rows outside the part are untouched
+    assert (out[~cov] == 7.0).all() and (lse[:, ~cov] == 7.0).all()
+    # merge mode: merging into (0, -inf) reproduces the partial; merging into a
+    # random running result matches the oracle merge
+    acc_o = torch.randn(out.shape, generator=g)
+    acc_l = torch.randn(lse.shape, generator=g)
+    acc_l[:, ::5] = float("-inf")
+    acc_o[::5] = 0.0
+    mo, ml = run_block(q, k, v, cu_q, cu_k, qp, kp, causal, merge_into=(acc_o, acc_l.clone()))
+    eo, el = oracle.lse_merge(to_np(acc_o), to_np(acc_l), ro, np.where(cov[None, :], rl, -np.inf))
+    check_out(mo[cov], eo[cov], "bf16", name + "/merge")
+    check_lse(ml[:, cov], el[:, cov], name + "/merge")
+    assert np.array_equal(mo[~cov], to_np(acc_o)[~cov])
+
+
+@pytest.mark.parametrize("case", EDGE_CASES, ids=[c[0] for c in EDGE_CASES])
+def test_block_fwd_fp32_edge_cases(case):
+    name, lq, lk, qp, kp, causal, hq, hkv = case
+    cu_q, cu_k = _cu(lq), _cu(lk)
+    g = torch.Generator().manual_seed(17)
+    q = torch.randn(int(cu_q[-1]), hq, 64, generator=g)
+    k = torch.randn(int(cu_k[-1]), hkv, 64, generator=g)
+    v = torch.randn(int(cu_k[-1]), hkv, 64, generator=g)
+    out, lse = run_block(q, k, v, cu_q, cu_k, qp, kp, causal)
+    ro, rl, cov = block_ref(to_np(q), to_np(k), to_np(v), cu_q, cu_k, qp, kp, causal)
+    check_out(out[cov], ro[cov], "fp32", name)
+    check_lse(lse[:, cov], rl[:, cov], name, tol=1e-5)
+    assert (out[~cov] == 7.0).all()
+
+
+# ---------------------------------------------------------------------------
+# bandwidth kernels
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows", [0, 1, 2])
+@pytest.mark.parametrize("dv", [128, 64, 192])
+def test_lse_merge_kernel(rows, dv):
+    lengths = [6, 0, 130, 64, 2]
+    cu = _cu(lengths)
+    T, H = int(cu[-1]), 3
+    g = torch.Generator().manual_seed(5 + rows)
+    oa = torch.randn(T, H, dv, generator=g)
+    ob = torch.randn(T, H, dv, generator=g)
+    la = torch.randn(H, T, generator=g) * 4
+    lb = torch.randn(H, T, generator=g) * 4
+    la[:, ::3] = float("-inf")
+    lb[:, ::4] = float("-inf")
+    oa[::3] = 0.0
+    ob[::4] = 0.0
+    la[:, 7] = 300.0
+    lb[:, 7] = 301.0                       # exp would overflow without the max factor
+    da, dla = oa.clone().to(DEV), la.clone().to(DEV)
+    L.ra_lse_merge(da, dla, ob.to(DEV), lb.to(DEV), torch.from_numpy(cu).to(DEV), cu, rows)
+    torch.cuda.synchronize()
+    eo, el = oracle.lse_merge(to_np(oa), to_np(la), to_np(ob), to_np(lb))
+    cov = np.zeros(T, bool)
+    for s in range(len(cu) - 1):
+        a, b = _part(cu[s], cu[s + 1], rows)
+        cov[a:b] = True
+    go, gl = to_np(da), to_np(dla)
+    assert metrics(go[cov], eo[cov])[0] <= 1e-5
+    # float32 lse near 300 has an ulp of 3e-5: compare relative to the magnitude
+    fin = np.isfinite(el[:, cov])
+    assert np.array_equal(np.isneginf(gl[:, cov]), np.isneginf(el[:, cov]))
+    rel = np.abs(gl[:, cov][fin] - el[:, cov][fin]) / np.maximum(1.0, np.abs(el[:, cov][fin]))
+    assert rel.max() <= 1e-6
+    assert np.array_equal(go[~cov], to_np(oa)[~cov])
+    assert np.array_equal(gl[:, ~cov], to_np(la)[:, ~cov])
+
+
+def test_cast_kernel_is_round_to_nearest_even():
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn(1 << 16, generator=g) * torch.exp(torch.randn(1 << 16, generator=g) * 20)
+    ties = torch.tensor([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), float("inf"),
+                         float("-inf"), 0.0, -0.0, 3.0e38], dtype=torch.float32)
+    x[:ties.numel()] = ties
+    y = torch.empty(x.numel(), dtype=torch.bfloat16, device=DEV)
+    L.ra_cast_f32_bf16(x.to(DEV), y)
+    torch.cuda.synchronize()
+    got = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, oracle.bf16_round_bits(x.numpy()))
+
+
+def test_zigzag_gather_scatter_exact():
+    from context_blockwise_softmax_ra_amd.ring import RingProblem
+    cu = _cu([32, 96, 8, 64])
+    T, C = int(cu[-1]), 4
+    x = torch.arange(T * 3 * 8, dtype=torch.float32).reshape(T, 3, 8).to(torch.bfloat16)
+    xd = x.to(DEV)
+    prob = RingProblem(xd, xd, xd, cu, C)
+    back = torch.zeros_like(xd)
+    for r in range(C):
+        idx, _ = oracle.zigzag_local_tokens(C, r, cu)
+        assert torch.equal(prob.q[r].cpu(), x[idx])
+        assert np.array_equal(prob.rows(r), idx)
+        prob.scatter(prob.q[r], back, r)
+    torch.cuda.synchronize()
+    assert torch.equal(back.cpu(), x)
+
+
+# ---------------------------------------------------------------------------
+# whole rank shares
+# ---------------------------------------------------------------------------
+
+def _run_all_ranks(prob, out_dtype, fuse):
+    outs, lses = [], []
+    for r in range(prob.cp):
+        out, lse, ws = prob.alloc_forward(out_dtype, fuse)
+        prob.forward(r, out, lse, ws, fuse_merge=fuse)
+        outs.append(out)
+        lses.append(lse)
+    torch.cuda.synchronize()
+    return [to_np(o) for o in outs], [to_np(l) for l in lses]
+
+
+def test_tiny_fp32_workload_steps_ranks_and_concat():
+    w = synth.WORKLOADS["tiny_fp32"]
+    prob, (q, k, v, _) = make_problem(w)
+    q64, k64, v64 = to_np(q), to_np(k), to_np(v)
+    cu = w.cu_global()
+    full_o, full_l = oracle.full_attention(q64, k64, v64, cu)
+    for fuse in (False, True):
+        outs, lses = _run_all_ranks(prob, torch.float32, fuse)
+        cat_o = np.zeros_like(full_o)
+        cat_l = np.zeros_like(full_l)
+        for r in range(w.cp):
+            ref = oracle.rank_share(q64, k64, v64, cu, w.cp, r)
+            check_out(outs[r], ref["out"], "fp32", f"rank{r} fuse={fuse}")
+            check_lse(lses[r], ref["lse"], f"rank{r}", tol=1e-5)
+            cat_o[prob.rows(r)] = outs[r]
+            cat_l[:, prob.rows(r)] = lses[r]
+        check_out(cat_o, full_o, "fp32", "concat==full")
+        check_lse(cat_l, full_l, "concat==full", tol=1e-5)
+    # every step's partial on its covered rows
+    for r in range(w.cp):
+        ref = oracle.rank_share(q64, k64, v64, cu, w.cp, r)
+        for s, (j, causal, qp, kp) in enumerate(prob.step_plan(r)):
+            owner, ro, rl = ref["steps"][s]
+            assert owner == j
+            d = prob.step_desc(r, j, causal, qp, kp)
+            out = torch.zeros((prob.Tl, w.hq, w.dv), dtype=torch.float32, device=DEV)
+            lse = torch.full((w.hq, prob.Tl), 7.0, dtype=torch.float32, device=DEV)
+            L.ra_block_attn_fwd(d, out, lse)
+            torch.cuda.synchronize()
+            go, gl = to_np(out), to_np(lse)
+            cov = gl[0] != 7.0
+            # the plan covers exactly the rows that see some key of the block
+            assert np.array_equal(cov, np.isfinite(rl[0]))
+            check_out(go[cov], ro[cov], "fp32", f"rank{r} step{s}")
+            check_lse(gl[:, cov], rl[:, cov], f"rank{r} step{s}", tol=1e-5)
+
+
+def _full_parity(w, fuse_modes=(False, True), determinism=False):
+    log(f"workload {w.name}: S={w.seqlen} C={w.cp} hq={w.hq} hkv={w.hkv} d={w.dqk}/{w.dv}")
+    prob, (q, k, v, _) = make_problem(w)
+    q64, k64, v64 = to_np(q), to_np(k), to_np(v)
+    ro, rl = oracle.full_attention(q64, k64, v64, w.cu_global())
+    for fuse in fuse_modes:
+        outs, lses = _run_all_ranks(prob, torch.bfloat16, fuse)
+        for r in range(w.cp):
+            rows = prob.rows(r)
+            check_out(outs[r], ro[rows], w.dtype, f"rank{r} fuse={fuse}")
+            check_lse(lses[r], rl[:, rows], f"rank{r} fuse={fuse}")
+        if determinism:
+            again, again_l = _run_all_ranks(prob, torch.bfloat16, fuse)
+            for r in range(w.cp):
+                assert np.array_equal(outs[r], again[r]) and np.array_equal(lses[r], again_l[r])
+    return prob
+
+
+def test_mha_8k_workload_full_parity():
+    _full_parity(synth.WORKLOADS["mha_8k"], determinism=True)
+
+
+def test_gqa_workload_reduced_full_parity():
+    _full_parity(synth.reduced("gqa_32k", 4096, 8))
+
+
+def test_varlen_workload_reduced_full_parity():
+    w = synth.reduced("varlen_128k", 16384, 4)
+    w.doc_lengths = synth.doc_lengths_loguniform(4, 16384, 8, 4096, 8)
+    _full_parity(w)
+
+
+def test_mla_forward_reduced_full_parity():
+    _full_parity(synth.reduced("mla_256k", 4096, 8))
+
+
+def _sampled_parity(w, ranks, n_rows=40, fuse=False):
+    log(f"workload {w.name} (full size, sampled rows): S={w.seqlen} C={w.cp}")
+    prob, (q, k, v, _) = make_problem(w)
+    q64 = to_np(q)
+    k64, v64 = to_np(k), to_np(v)
+    del q, k, v
+    cu = w.cu_global()
+    for r in ranks:
+        out, lse, ws = prob.alloc_forward(torch.bfloat16, fuse)
+        prob.forward(r, out, lse, ws, fuse_merge=fuse)
+        torch.cuda.synchronize()
+        loc = sample_rows(prob, r, n_rows)
+        glob = prob.rows(r)[loc]
+        ro, rl = oracle.full_attention(q64, k64, v64, cu, rows=glob)
+        check_out(to_np(out[torch.from_numpy(loc).to(DEV)]), ro, w.dtype, f"rank{r}")
+        check_lse(to_np(lse)[:, loc], rl, f"rank{r}")
+        del out, lse, ws
+    return prob
+
+
+def test_gqa_32k_workload_sampled():
+    _sampled_parity(synth.WORKLOADS["gqa_32k"], ranks=(0, 3, 7))
+
+
+def test_varlen_128k_workload_sampled():
+    _sampled_parity(synth.WORKLOADS["varlen_128k"], ranks=(0, 7, 15), fuse=True)
+
+
+def test_rank_accounting_matches_oracle_pairs():
+    for name in ("mha_8k", "gqa_32k", "varlen_128k"):
+        w = synth.WORKLOADS[name]
+        cu = w.cu_global()
+        from context_blockwise_softmax_ra_amd.ring import RingProblem
+        z = torch.zeros((w.seqlen, 1, 64), dtype=torch.bfloat16, device=DEV)
+        prob = RingProblem(z, z, z, cu, w.cp)
+        for r in (0, w.cp - 1):
+            # one head: the counts are per query head
+            pairs = sum(p for p, _, _ in prob.work(r))
+            assert pairs == oracle.visible_pairs(cu, w.cp, r), name
