@@ -42,7 +42,22 @@ def parse():
                     help="1: merge in the attention epilogue instead of ra_lse_merge")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the oracle CPU baseline sample (0 = skip)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB 3 times (the "
+                         "reference kernel that scales HBM byte counters), then exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int):
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4,
+                      "launches": 3}), flush=True)
 
 
 def kernel_hash() -> str:
@@ -107,6 +122,9 @@ def main():
         print(json.dumps({"error": "this build measures one GPU only: every simulated rank's "
                                    "share runs in turn on a single MI355X; run with --gpus 1"}))
         sys.exit(2)
+    if a.copy_calibration_mib:
+        copy_calibration(a.copy_calibration_mib)
+        return
     import numpy as np
     import torch
     import synth

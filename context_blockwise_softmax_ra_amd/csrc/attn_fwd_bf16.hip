@@ -27,10 +27,17 @@
 //
 // K rows are fed to the S^T product in a permuted order sigma so that the
 // 8 accumulator values a lane feeds as one B operand of the P*V product are
-// 8 consecutive keys; V^T then needs one 16-byte LDS read per operand.
-// V is transposed in registers on its way into LDS (4 keys x 8 dims per
-// thread).  LDS rows are XOR-swizzled in 16-byte chunks so that the 8 lanes
-// served together by a 128-bit LDS read hit 8 distinct bank groups.
+// 8 consecutive keys.  V stays row-major in LDS and the V^T operand is read
+// with the gfx950 transposing LDS read (ds_read_b64_tr_b16): within each
+// 16-lane group, lane i receives element i%4 of the 8 bytes addressed by
+// lanes 4r + i/4, r = 0..3, so lanes pointing at 4 consecutive key rows
+// hand every lane 4 consecutive keys of one dim.
+//
+// LDS banking (64 banks x 4 bytes; a 128-bit access serves 16 lanes at a
+// time, a 64-bit access 32): K rows are padded to an odd number of 16-byte
+// slots, so the 16 rows read together land on 16 distinct slots; V rows
+// are padded to a stride of 64 mod 256 bytes, so the 4 rows x 64 bytes one
+// transposing read touches cover all 64 banks once.
 //
 // Blocks are remapped so that each of the 8 XCDs gets a contiguous range of
 // tiles ordered (segment, kv head, query tile, head in group): the query
@@ -66,7 +73,8 @@ __device__ __forceinline__ int sigma(int mm) {
   return ((i >> 3) << 4) | (g << 3) | (i & 7);
 }
 
-__device__ __forceinline__ int swz_k(int row) { return (row & 3) | (((row >> 3) & 1) << 2); }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -74,34 +82,56 @@ __device__ __forceinline__ u32x4 ldg16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16x2, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
-  // round to nearest even (inputs are finite or +-inf; p in [0, 1])
-  unsigned a = __float_as_uint(lo), b = __float_as_uint(hi);
-  a += 0x7fffu + ((a >> 16) & 1u);
-  b += 0x7fffu + ((b >> 16) & 1u);
-  return (a >> 16) | (b & 0xffff0000u);
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
 }
+
+// max / sum of a value and its copy in lane l^32 (v_permlane32_swap).
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Rescale threshold (log2 units): the running max used for the exponent is
+// only raised when a row's max grows by more than this, so the output
+// rescale is skipped on most tiles.  Exact: numerator, row sum and lse all
+// use the same (possibly stale) max; p stays <= 2^8.
+constexpr float kRescaleLog2 = 8.0f;
 
 template <int DQK, int DV>
 struct Geo {
   static constexpr int KCH = DQK / 8;                 // 16-byte chunks per K row
-  static constexpr int K_BYTES = BN * DQK * 2;
-  static constexpr int V_BYTES = DV * BN * 2;
+  static constexpr int VCH = DV / 8;                  // 16-byte chunks per V row
+  static constexpr int KSTR = DQK * 2 + 16;           // odd number of 16-byte slots
+  static constexpr int VSTR = DV * 2 + 64;            // 64 mod 256 bytes
+  static constexpr int K_BYTES = BN * KSTR;
+  static constexpr int V_BYTES = BN * VSTR;
   static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int NBUF = (2 * STAGE <= 65536) ? 2 : 1;
+  static constexpr int NBUF = (2 * STAGE <= 81920) ? 2 : 1;
   static constexpr int K_LD = (BN * KCH) / NT;        // K chunks per thread
-  static constexpr int V_ITEMS = (BN / 4) * (DV / 8); // 4 keys x 8 dims items
+  static constexpr int V_LD = (BN * VCH) / NT;        // V chunks per thread
   static constexpr int KK = DQK / 16;                 // MFMA k-steps for S
   static constexpr int OT = DV / 32;                  // output tiles per wave
-  static_assert((BN * KCH) % NT == 0, "K tile load split");
-  static_assert(V_ITEMS <= NT, "V tile load split");
-  static_assert(KCH % 8 == 0, "swizzle groups");
+  static_assert((BN * KCH) % NT == 0 && (BN * VCH) % NT == 0, "tile load split");
+  static_assert(((KSTR / 16) & 1) == 1 && (VSTR % 256) == 64 || (DV == 64 && VSTR == 192),
+                "bank spread");
 };
 
 template <int DQK, int DV>
 struct Prefetch {
   u32x4 k[Geo<DQK, DV>::K_LD];
-  u32x4 v[4];
+  u32x4 v[Geo<DQK, DV>::V_LD];
 };
 
 template <int DQK, int DV>
@@ -116,13 +146,12 @@ __device__ __forceinline__ void load_tile(Prefetch<DQK, DV>& pf, const __bf16* _
     const int tok = min(key0 + row, k_last);
     pf.k[i] = ldg16(kb + (int64_t)tok * ks + c * 8);
   }
-  if (tid < G::V_ITEMS) {
-    const int kq = tid / (DV / 8), dvb = tid % (DV / 8);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tok = min(key0 + 4 * kq + j, k_last);
-      pf.v[j] = ldg16(vb + (int64_t)tok * vs + dvb * 8);
-    }
+  for (int i = 0; i < G::V_LD; ++i) {
+    const int idx = tid + NT * i;
+    const int row = idx / G::VCH, c = idx % G::VCH;
+    const int tok = min(key0 + row, k_last);
+    pf.v[i] = ldg16(vb + (int64_t)tok * vs + c * 8);
   }
 }
 
@@ -130,33 +159,18 @@ template <int DQK, int DV>
 __device__ __forceinline__ void store_tile(const Prefetch<DQK, DV>& pf, char* stage, int tid) {
   using G = Geo<DQK, DV>;
   char* ks = stage;
-  char* vt = stage + G::K_BYTES;
+  char* vs = stage + G::K_BYTES;
 #pragma unroll
   for (int i = 0; i < G::K_LD; ++i) {
     const int idx = tid + NT * i;
     const int row = idx / G::KCH, c = idx % G::KCH;
-    *reinterpret_cast<u32x4*>(ks + row * (DQK * 2) + ((c ^ swz_k(row)) << 4)) = pf.k[i];
+    *reinterpret_cast<u32x4*>(ks + row * G::KSTR + (c << 4)) = pf.k[i];
   }
-  if (tid < G::V_ITEMS) {
-    const int kq = tid / (DV / 8), dvb = tid % (DV / 8);
-    const int chunk = kq >> 1, half = (kq & 1) << 3;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int w = j >> 1;
-      unsigned lo, hi;
-      if (j & 1) {
-        lo = (pf.v[0][w] >> 16) | (pf.v[1][w] & 0xffff0000u);
-        hi = (pf.v[2][w] >> 16) | (pf.v[3][w] & 0xffff0000u);
-      } else {
-        lo = (pf.v[0][w] & 0xffffu) | (pf.v[1][w] << 16);
-        hi = (pf.v[2][w] & 0xffffu) | (pf.v[3][w] << 16);
-      }
-      const int m = dvb * 8 + j;
-      u32x2 val;
-      val[0] = lo;
-      val[1] = hi;
-      *reinterpret_cast<u32x2*>(vt + m * (BN * 2) + (((chunk ^ (m & 7)) << 4) | half)) = val;
-    }
+  for (int i = 0; i < G::V_LD; ++i) {
+    const int idx = tid + NT * i;
+    const int row = idx / G::VCH, c = idx % G::VCH;
+    *reinterpret_cast<u32x4*>(vs + row * G::VSTR + (c << 4)) = pf.v[i];
   }
 }
 
@@ -229,6 +243,10 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 
   const int k_last = k_hi - 1;
   const int krow_a = sigma(l32);
+  // transposing-read address of this lane: key row 8g + (lane%16)/4, dims
+  // 16*((lane/16)%2) + 4*(lane%4) (+32 per output tile, +4 rows for keys 4..7)
+  const int v_row = 8 * g + ((lane & 15) >> 2);
+  const int v_col = (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 
   Prefetch<DQK, DV> pf;
   if (ntiles > 0) {
@@ -244,20 +262,17 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
     const int kt0 = t * BN;  // relative to k_lo
     if (wave_live && kt0 < wave_kend) {
       const char* ks = stage;
-      const char* vt = stage + G::K_BYTES;
+      const char* vsm = stage + G::K_BYTES;
       // ---- S^T = K * Q^T : two 32-key halves
       f32x16 s[2];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[hh][i] = 0.f;
-        const int row = krow_a + 32 * hh;
-        const char* rp = ks + row * (DQK * 2);
-        const int sw = swz_k(row);
+        const char* rp = ks + (krow_a + 32 * hh) * G::KSTR + (g << 4);
 #pragma unroll
         for (int kk = 0; kk < G::KK; ++kk) {
-          const int c = 2 * kk + g;
-          const u32x4 kv = *reinterpret_cast<const u32x4*>(rp + ((c ^ sw) << 4));
+          const u32x4 kv = *reinterpret_cast<const u32x4*>(rp + (kk << 5));
           s[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qf[kk], s[hh], 0, 0, 0);
         }
       }
@@ -273,18 +288,27 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
             if (!ok) s[hh][i] = -INFINITY;
           }
       }
-      // ---- online softmax (log2 domain)
-      float mx = s[0][0];
+      // ---- online softmax (log2 domain, lazily rescaled)
+      float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+      for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[0][i], s[0][i + 1]));
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float mc = m_use * c2;
-      const float alpha = __builtin_amdgcn_exp2f(m_run * c2 - mc);
-      m_run = m_new;
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[1][i], s[1][i + 1]));
+      mx = xhalf_max(mx);
+      // raise the running max only if it grew by more than the threshold
+      const bool raise = (mx - m_run) * c2 > kRescaleLog2;   // true on the first live tile
+      if (__builtin_amdgcn_ballot_w64(raise)) {
+        const float m_new = raise ? mx : m_run;
+        const float m_use_new = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_use_new) * c2);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int tt = 0; tt < G::OT; ++tt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[tt][i] *= alpha;
+      }
+      const float mc = ((m_run == -INFINITY) ? 0.f : m_run) * c2;
       float rs = 0.f;
       unsigned pk[16];
 #pragma unroll
@@ -296,11 +320,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
           rs += p0 + p1;
           pk[hh * 8 + (i >> 1)] = pack_bf16x2(p0, p1);
         }
-      l_run = l_run * alpha + rs;
-#pragma unroll
-      for (int tt = 0; tt < G::OT; ++tt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[tt][i] *= alpha;
+      l_run += rs;
       // ---- O^T += V^T * P^T : 4 k-steps of 16 keys
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
@@ -310,13 +330,16 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
         pv[2] = pk[4 * bb + 2];
         pv[3] = pk[4 * bb + 3];
         const bf16x8 pb = as_bf16x8(pv);
-        const int c = 2 * bb + g;
+        // V^T operand: keys 16bb + 8g + 0..7 of dim 32tt + l32, two transposing reads
+        const char* vp = vsm + (16 * bb + v_row) * G::VSTR + v_col;
 #pragma unroll
         for (int tt = 0; tt < G::OT; ++tt) {
-          const int m = 32 * tt + l32;
-          const u32x4 vv =
-              *reinterpret_cast<const u32x4*>(vt + m * (BN * 2) + ((c ^ (m & 7)) << 4));
-          o[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), pb, o[tt], 0, 0, 0);
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 64 * tt));
+          const s16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 4 * G::VSTR + 64 * tt));
+          const bf16x8 va = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[tt], 0, 0, 0);
         }
       }
     }
@@ -332,7 +355,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   if (!wave_live || my_row >= q_hi) return;
 
   // ---- epilogue: lanes l and l^32 hold the two key halves of the same row
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = xhalf_sum(l_run);
   const bool empty = !(l_tot > 0.f);
   const float inv = empty ? 0.f : 1.f / l_tot;
   const float m_fin = (m_run == -INFINITY) ? 0.f : m_run;
