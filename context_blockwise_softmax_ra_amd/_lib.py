@@ -129,13 +129,27 @@ def _check(status: int):
         raise RaError(status, lib().ra_last_error().decode())
 
 
-def _ptr(t) -> Optional[int]:
+def _ptr(t, token_strided: bool = False) -> Optional[int]:
+    """Address of a buffer; tensors must be dense (the C ABI takes no strides).
+
+    ``token_strided``: a [tokens, heads, dim] tensor whose token stride is
+    passed separately; heads and dim must still be packed.
+    """
     if t is None:
         return None
     if isinstance(t, int):
         return t
     if isinstance(t, np.ndarray):
+        if not t.flags["C_CONTIGUOUS"]:
+            raise ValueError("host array must be C-contiguous")
         return t.ctypes.data
+    if token_strided:
+        if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+            raise ValueError(f"[tokens, heads, dim] tensor needs packed heads/dim, got "
+                             f"shape {tuple(t.shape)} strides {t.stride()}")
+    elif not t.is_contiguous():
+        raise ValueError(f"tensor must be contiguous, got shape {tuple(t.shape)} strides "
+                         f"{t.stride()}")
     return t.data_ptr()
 
 
@@ -172,7 +186,7 @@ def attn_desc(q, k, v, cu_q, cu_k, cu_q_host, cu_k_host, *, q_part=PART_ALL,
     """
     ref = q if q is not None else k
     d = AttnDesc()
-    d.q, d.k, d.v = _ptr(q), _ptr(k), _ptr(v)
+    d.q, d.k, d.v = _ptr(q, True), _ptr(k, True), _ptr(v, True)
     d.dtype = _dtype_code(ref) if dtype is None else dtype
     d.hq = q.shape[1] if q is not None else 0
     d.hkv = k.shape[1] if k is not None else d.hq

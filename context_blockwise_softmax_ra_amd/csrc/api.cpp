@@ -478,6 +478,7 @@ static ra_status launch_bwd(const ra_attn_desc* d, const Checked& c, const void*
                             const float* lse, const float* delta, float* dq, float* dk, float* dv,
                             hipStream_t st) {
   ra::AttnArgs a = make_args(d, c);
+  a.n_ktiles = (c.max_k_part + 127) / 128;  // 128-key tiles of the dK/dV kernel
   a.dout = dout;
   a.lse_in = lse;
   a.delta = delta;

@@ -1,0 +1,116 @@
+// Device helpers shared by the bf16 attention kernels (forward and backward).
+//
+// Matrix-core layout used throughout (v_mfma_f32_32x32x16_bf16, wave64):
+//   A operand (M x K = 32 x 16): lane l holds row l%32, k = 8*(l/32) .. +7
+//   B operand (K x N = 16 x 32): lane l holds column l%32, k = 8*(l/32) .. +7
+//   C/D (32 x 32 fp32, 16 per lane): lane l holds column l%32 and rows
+//       8*(i/4) + 4*(l/32) + i%4 for i = 0..15.
+#pragma once
+
+#include "ra_internal.h"
+
+namespace ra {
+namespace mfma {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ __forceinline__ u32x4 lds16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Two floats -> packed bf16x2, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+}
+
+// 8 accumulator entries [i0, i0+8) of a C tile as a bf16x8 MFMA operand.
+__device__ __forceinline__ bf16x8 pack8(const f32x16& c, int i0) {
+  u32x4 u;
+  u[0] = pack_bf16x2(c[i0 + 0], c[i0 + 1]);
+  u[1] = pack_bf16x2(c[i0 + 2], c[i0 + 3]);
+  u[2] = pack_bf16x2(c[i0 + 4], c[i0 + 5]);
+  u[3] = pack_bf16x2(c[i0 + 6], c[i0 + 7]);
+  return as_bf16x8(u);
+}
+
+// Value exchange with lane l^32 (v_permlane32_swap).
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Row fed as A-operand row mm so that C entries 8j..8j+7 of a lane are 8
+// consecutive rows of that operand: entry i of lane l is row
+// 16*(i/8) + 8*(l/32) + i%8.
+__device__ __forceinline__ int sigma(int mm) {
+  const int g = (mm >> 2) & 1;
+  const int i = ((mm >> 3) << 2) | (mm & 3);
+  return ((i >> 3) << 4) | (g << 3) | (i & 7);
+}
+
+// Blocks are dispatched round-robin over the 8 XCDs (b % 8); give each XCD
+// a contiguous range of logical tiles so neighbours share its L2.
+__device__ __forceinline__ int xcd_remap(int b, int nb) {
+  const int q = nb >> 3, r = nb & 7, x = b & 7;
+  return x * q + (x < r ? x : r) + (b >> 3);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group,
+// lane i receives element i%4 of the 8 bytes addressed by lane 4r + i/4,
+// r = 0..3.
+__device__ __forceinline__ s16x4 lds_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+}
+__device__ __forceinline__ bf16x8 cat_tr(s16x4 lo, s16x4 hi) {
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// "Dual" LDS tile layout for tiles read both by 128-bit row reads (16 rows
+// at one 16-byte chunk) and by transposing reads (4 consecutive rows x 64
+// bytes): rows of ROWB = 256 or 512 bytes, 16-byte chunks XOR-swizzled by
+// swz(row) within each 256-byte half.  Both patterns then touch 16
+// distinct chunk slots of the 64 banks.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+template <int ROWB>
+__device__ __forceinline__ int dual_off(int row, int byte) {
+  return row * ROWB + ((((byte >> 4) ^ swz(row))) << 4) + (byte & 15);
+}
+
+// Byte column, within a 32-column tile of 16-bit elements, that lane
+// addresses in a transposing read: 16*((lane/16)%2) + 4*(lane%4) elements.
+__device__ __forceinline__ int tr_col_bytes(int lane) {
+  return (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+}
+// Row, within the 16-row k-step, that lane addresses in a transposing read
+// for k = 8*(lane/32) .. +3 (add 4 for the next 4).
+__device__ __forceinline__ int tr_row(int lane) { return 8 * (lane >> 5) + ((lane & 15) >> 2); }
+
+}  // namespace mfma
+}  // namespace ra

@@ -227,3 +227,17 @@ def test_work_accounting_matches_oracle_pairs(lengths, C, hq):
             tot += pairs
             assert vis >= 0 and skip >= 0
         assert tot == hq * oracle.visible_pairs(cu, C, r)
+
+
+def test_binding_rejects_non_contiguous_buffers():
+    import torch
+    x = torch.zeros(4, 6).t()                   # transposed view
+    with pytest.raises(ValueError):
+        L._ptr(x)
+    q = torch.zeros(8, 4, 16)[:, ::2, :]         # heads not packed
+    with pytest.raises(ValueError):
+        L._ptr(q, True)
+    ok = torch.zeros(8, 6, 16)[:, :4, :]         # token-strided view is fine
+    assert L._ptr(ok, True) == ok.data_ptr()
+    with pytest.raises(ValueError):
+        L._ptr(np.zeros((3, 4)).T)

@@ -1,0 +1,206 @@
+"""GPU parity of the backward path (recompute from the saved lse) against the fp64 oracle.
+
+Block level: dQ, dK, dV of one block (segments, halves, causal) with the
+oracle's own lse and delta as inputs.  Rank level: every simulated rank's
+backward share (its dQ, and dK/dV added into the KV owner's buffers), the
+concatenation compared with the un-sharded gradients.  At the 256K MLA
+shape: sampled dQ rows, dK/dV of the last 256 keys, and the sum rules
+sum_j dV_j = sum_i dO_i and sum_j dK_j = 0.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import check_out, log, make_problem, metrics, sample_rows, to_np
+
+pytestmark = pytest.mark.gpu
+
+R = pytest.importorskip("context_blockwise_softmax_ra_amd")
+from context_blockwise_softmax_ra_amd import _lib as L  # noqa: E402
+
+DEV = torch.device("cuda:0")
+
+
+def _part(a, b, part):
+    h = (b - a) // 2
+    return (a, a + h) if part == 1 else ((a + h, b) if part == 2 else (a, b))
+
+
+def block_bwd_ref(q, k, v, do, cu_q, cu_k, qp, kp, causal):
+    """Oracle gradients of one block treated as the whole attention of its rows."""
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    lse = np.full((q.shape[1], q.shape[0]), -np.inf)
+    out = np.zeros((q.shape[0], q.shape[1], v.shape[2]))
+    for s in range(len(cu_q) - 1):
+        q0, q1 = _part(cu_q[s], cu_q[s + 1], qp)
+        k0, k1 = _part(cu_k[s], cu_k[s + 1], kp)
+        if q1 <= q0 or k1 <= k0:
+            continue
+        qpos, kpos = np.arange(q1 - q0), np.arange(k1 - k0)
+        z1, z2 = np.zeros_like(qpos), np.zeros_like(kpos)
+        o, l = oracle.attention(q[q0:q1], k[k0:k1], v[k0:k1], qpos, z1, kpos, z2, causal=causal)
+        a, b, c = oracle.attention_bwd(q[q0:q1], k[k0:k1], v[k0:k1], do[q0:q1], qpos, z1, kpos,
+                                       z2, causal=causal, out=o, lse=l)
+        dq[q0:q1] += a
+        dk[k0:k1] += b
+        dv[k0:k1] += c
+        out[q0:q1] = o
+        lse[:, q0:q1] = l
+    return dq, dk, dv, out, lse
+
+
+CASES = [
+    ("ragged_causal", [333], [333], 0, 0, True, 4, 2),
+    ("multi_seg_noncausal", [5, 0, 130, 64, 1], [9, 3, 200, 1, 64], 0, 0, False, 2, 2),
+    ("causal_tiny_segs", [1, 2, 129, 64, 63, 300], [1, 2, 129, 64, 63, 300], 0, 0, True, 2, 1),
+    ("halves_q2_kall", [2, 300, 130, 0], [2, 300, 130, 0], 2, 0, False, 4, 4),
+    ("halves_qall_k1", [2, 300, 130, 256], [2, 300, 130, 256], 0, 1, False, 4, 1),
+    ("empty_keys", [64, 70], [0, 5], 0, 0, False, 2, 2),
+]
+
+
+@pytest.mark.parametrize("dims", [(128, 128), (192, 128)])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_block_bwd_edge_cases(case, dims):
+    name, lq, lk, qp, kp, causal, hq, hkv = case
+    dqk, dv = dims
+    log(f"case {name} dims {dims}")
+    cu_q, cu_k = synth.cu_seqlens(lq), synth.cu_seqlens(lk)
+    g = torch.Generator().manual_seed(11 + len(name) + dqk)
+    Tq, Tk = int(cu_q[-1]), int(cu_k[-1])
+    q = torch.randn(Tq, hq, dqk, generator=g).to(torch.bfloat16)
+    k = torch.randn(Tk, hkv, dqk, generator=g).to(torch.bfloat16)
+    v = torch.randn(Tk, hkv, dv, generator=g).to(torch.bfloat16)
+    do = torch.randn(Tq, hq, dv, generator=g).to(torch.bfloat16)
+    rq, rk, rv, ro, rl = block_bwd_ref(to_np(q), to_np(k), to_np(v), to_np(do), cu_q, cu_k,
+                                       qp, kp, causal)
+    delta = oracle.bwd_delta(ro, to_np(do))
+    dq_d, dk_d, dv_d = (q.to(DEV), k.to(DEV), v.to(DEV))
+    cuq = torch.from_numpy(cu_q).to(DEV)
+    cuk = torch.from_numpy(cu_k).to(DEV)
+    desc = L.attn_desc(dq_d, dk_d, dv_d, cuq, cuk, cu_q, cu_k, q_part=qp, k_part=kp,
+                       causal=causal)
+    gq = torch.full((Tq, hq, dqk), 0.25, device=DEV)          # accumulators are added to
+    gk = torch.full((Tk, hkv, dqk), -0.5, device=DEV)
+    gv = torch.full((Tk, hkv, dv), 0.125, device=DEV)
+    lse_t = torch.from_numpy(np.ascontiguousarray(rl, dtype=np.float32)).to(DEV)
+    delta_t = torch.from_numpy(np.ascontiguousarray(delta, dtype=np.float32)).to(DEV)
+    L.ra_block_attn_bwd(desc, do.to(DEV), lse_t, delta_t, gq, gk, gv)
+    torch.cuda.synchronize()
+    check_out(to_np(gq) - 0.25, rq, "bf16", f"{name} dQ")
+    check_out(to_np(gk) + 0.5, rk, "bf16", f"{name} dK")
+    check_out(to_np(gv) - 0.125, rv, "bf16", f"{name} dV")
+
+
+def _run_ranks(prob, with_fwd_fuse=True):
+    """Forward every rank, then backward every rank; returns dq per rank, dk/dv per owner."""
+    outs, lses = [], []
+    for r in range(prob.cp):
+        out, lse, ws = prob.alloc_forward(torch.bfloat16, with_fwd_fuse)
+        prob.forward(r, out, lse, ws, fuse_merge=with_fwd_fuse)
+        outs.append(out)
+        lses.append(lse)
+    dqs = [torch.zeros((prob.Tl, prob.hq, prob.dqk), device=DEV) for _ in range(prob.cp)]
+    dks = [torch.zeros((prob.Tl, prob.hkv, prob.dqk), device=DEV) for _ in range(prob.cp)]
+    dvs = [torch.zeros((prob.Tl, prob.hkv, prob.dv), device=DEV) for _ in range(prob.cp)]
+    n = L.ra_rank_backward_workspace(prob.backward_desc(0, outs[0], lses[0], dqs[0], dks, dvs, None))
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+    for r in range(prob.cp):
+        prob.backward(r, outs[r], lses[r], dqs[r], dks, dvs, ws)
+    torch.cuda.synchronize()
+    return outs, lses, dqs, dks, dvs
+
+
+def _full_bwd_parity(w):
+    log(f"workload {w.name}: S={w.seqlen} C={w.cp} hq={w.hq} hkv={w.hkv} d={w.dqk}/{w.dv}")
+    prob, (q, k, v, do) = make_problem(w, with_dout=True)
+    q64, k64, v64, do64 = to_np(q), to_np(k), to_np(v), to_np(do)
+    cu = w.cu_global()
+    lay = oracle.ref.Layout(cu)
+    rq, rk, rv = oracle.attention_bwd(q64, k64, v64, do64, lay.pos, lay.doc, lay.pos, lay.doc)
+    _, _, dqs, dks, dvs = _run_ranks(prob)
+    gq = np.zeros_like(rq)
+    gk = np.zeros_like(rk)
+    gv = np.zeros_like(rv)
+    for r in range(w.cp):
+        rows = prob.rows(r)
+        gq[rows] = to_np(dqs[r])
+        gk[rows] = to_np(dks[r])
+        gv[rows] = to_np(dvs[r])
+    check_out(gq, rq, "bf16", "dQ")
+    check_out(gk, rk, "bf16", "dK")
+    check_out(gv, rv, "bf16", "dV")
+
+
+def test_mla_backward_reduced_full_parity():
+    _full_bwd_parity(synth.reduced("mla_256k", 4096, 8))
+
+
+def test_gqa_backward_reduced_full_parity():
+    _full_bwd_parity(synth.reduced("gqa_32k", 4096, 8))
+
+
+def test_mha_backward_reduced_full_parity():
+    _full_bwd_parity(synth.reduced("mha_8k", 2048, 4))
+
+
+def test_varlen_backward_reduced_full_parity():
+    w = synth.reduced("varlen_128k", 8192, 4)
+    w.doc_lengths = synth.doc_lengths_loguniform(4, 8192, 8, 2048, 8)
+    _full_bwd_parity(w)
+
+
+def test_backward_is_deterministic():
+    w = synth.reduced("mla_256k", 2048, 4)
+    prob, _ = make_problem(w, with_dout=True)
+    a = _run_ranks(prob)
+    b = _run_ranks(prob)
+    for x, y in zip(a[2] + a[3] + a[4], b[2] + b[3] + b[4]):
+        assert torch.equal(x, y)
+
+
+def test_mla_256k_backward_sampled_and_sum_rules():
+    w = synth.WORKLOADS["mla_256k"]
+    log(f"workload {w.name} (full size): S={w.seqlen} C={w.cp}")
+    prob, (q, k, v, do) = make_problem(w, with_dout=True)
+    outs, lses, dqs, dks, dvs = _run_ranks(prob)
+    cu = w.cu_global()
+    lay = oracle.ref.Layout(cu)
+    q64, k64, v64, do64 = to_np(q), to_np(k), to_np(v), to_np(do)
+    del q, k, v, do
+    # sum rules over the whole sequence
+    sdv = sum(to_np(x).sum(0) for x in dvs)                # [hkv, dv]
+    sdo = do64.sum(0)                                       # [hq, dv] (hq == hkv here)
+    rel = np.abs(sdv - sdo).max() / np.abs(sdo).max()
+    log(f"  sum dV vs sum dO rel={rel:.2e}")
+    assert rel <= 1e-3
+    sdk = sum(to_np(x).sum(0) for x in dks)
+    adk = sum(np.abs(to_np(x)).sum(0) for x in dks)
+    rel = np.abs(sdk).max() / adk.max()
+    log(f"  |sum dK| / sum|dK| = {rel:.2e}")
+    assert rel <= 1e-3
+    # sampled dQ rows of ranks 0, 15, 31
+    for r in (0, 15, 31):
+        loc = sample_rows(prob, r, 24, seed=7)
+        rows = prob.rows(r)[loc]
+        o, l = oracle.attention(q64[rows], k64, v64, lay.pos[rows], lay.doc[rows], lay.pos, lay.doc)
+        a, _, _ = oracle.attention_bwd(q64[rows], k64, v64, do64[rows], lay.pos[rows],
+                                       lay.doc[rows], lay.pos, lay.doc, out=o, lse=l)
+        check_out(to_np(dqs[r])[loc], a, "bf16", f"rank{r} dQ rows")
+    # dK, dV of the last 256 keys: only the last 256 rows (rank 0's last chunk) see them
+    S = w.seqlen
+    rows = np.arange(S - 256, S)
+    keys = np.arange(S - 256, S)
+    o, l = oracle.attention(q64[rows], k64, v64, lay.pos[rows], lay.doc[rows], lay.pos, lay.doc)
+    _, rk, rv = oracle.attention_bwd(q64[rows], k64[keys], v64[keys], do64[rows], lay.pos[rows],
+                                     lay.doc[rows], lay.pos[keys], lay.doc[keys], out=o, lse=l,
+                                     delta=oracle.bwd_delta(o, do64[rows]))
+    r0 = prob.rows(0)
+    loc = np.searchsorted(r0, keys)
+    assert np.array_equal(r0[loc], keys)
+    check_out(to_np(dks[0])[loc], rk, "bf16", "last-256 dK")
+    check_out(to_np(dvs[0])[loc], rv, "bf16", "last-256 dV")
