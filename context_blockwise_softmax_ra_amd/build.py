@@ -34,9 +34,18 @@ def sources():
     return out
 
 
+# Per-file flags.  The attention kernels take row maxima of matrix-core
+# outputs; without this, IEEE-mode fmaxf canonicalises every operand first
+# (one extra v_max_f32 per score).  NaN inputs still propagate to NaN outputs.
+PER_FILE = {
+    "attn_fwd_bf16.hip": ["-fno-honor-nans"],
+    "attn_bwd_bf16.hip": ["-fno-honor-nans"],
+}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + COMMON + ["-c", src, "-o", obj]
+    cmd = [HIPCC] + COMMON + PER_FILE.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

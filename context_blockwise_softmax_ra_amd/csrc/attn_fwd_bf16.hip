@@ -28,80 +28,35 @@
 // K rows are fed to the S^T product in a permuted order sigma so that the
 // 8 accumulator values a lane feeds as one B operand of the P*V product are
 // 8 consecutive keys.  V stays row-major in LDS and the V^T operand is read
-// with the gfx950 transposing LDS read (ds_read_b64_tr_b16): within each
-// 16-lane group, lane i receives element i%4 of the 8 bytes addressed by
-// lanes 4r + i/4, r = 0..3, so lanes pointing at 4 consecutive key rows
-// hand every lane 4 consecutive keys of one dim.
+// with the gfx950 transposing LDS read (ds_read_b64_tr_b16).
 //
-// LDS banking (64 banks x 4 bytes; a 128-bit access serves 16 lanes at a
-// time, a 64-bit access 32): K rows are padded to an odd number of 16-byte
-// slots, so the 16 rows read together land on 16 distinct slots; V rows
-// are padded to a stride of 64 mod 256 bytes, so the 4 rows x 64 bytes one
-// transposing read touches cover all 64 banks once.
+// K/V tiles go from global memory straight into LDS (global_load_lds_dwordx4:
+// each wave instruction fills 1 KiB of LDS, lane i writing bytes 16i..16i+15),
+// double-buffered: tile t+1 streams in while tile t is computed, with one
+// barrier per tile.  Because the LDS destination of a lane is fixed, bank
+// spreading is done by choosing which global 16-byte chunk each lane
+// fetches (an XOR swizzle), with 64 banks x 4 bytes in mind:
+//   K: 64-dim panels of 128-byte rows, chunk slot = chunk ^ ((row>>1)&7);
+//      the 16 rows a 128-bit read serves at once land on 16 distinct slots.
+//   V: 256-byte rows, chunk slot = chunk ^ (((row&3)<<2)|((row>>2)&3)); the
+//      4 rows x 64 bytes of one transposing read land on 16 distinct slots.
 //
 // Blocks are remapped so that each of the 8 XCDs gets a contiguous range of
 // tiles ordered (segment, kv head, query tile, head in group): the query
 // heads sharing a kv head, and neighbouring query tiles, read the same K/V
 // through the same L2.  Causal launches order query tiles heaviest first.
 
-#include "ra_internal.h"
+#include "mfma_common.h"
 
 namespace ra {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+using namespace mfma;
 
 constexpr int BM = kFwdBlockM;
 constexpr int BN = kFwdBlockN;
-constexpr int NT = kFwdWaves * 64;
-
-__device__ __forceinline__ int xcd_remap(int b, int nb) {
-  // Hardware places block b on XCD b % 8.  Hand XCD x the logical range
-  // [x*q + min(x, r), ...) so consecutive logical tiles share an L2.
-  const int q = nb >> 3, r = nb & 7, x = b & 7;
-  return x * q + (x < r ? x : r) + (b >> 3);
-}
-
-// Key row fed by accumulator row mm so that accumulator entries
-// 8j..8j+7 of a lane hold 8 consecutive keys (see file comment).
-__device__ __forceinline__ int sigma(int mm) {
-  const int g = (mm >> 2) & 1;
-  const int i = ((mm >> 3) << 2) | (mm & 3);
-  return ((i >> 3) << 4) | (g << 3) | (i & 7);
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-__device__ __forceinline__ u32x4 ldg16(const void* p) {
-  return *reinterpret_cast<const u32x4*>(p);
-}
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// Two floats -> packed bf16x2, round to nearest even (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
-  f32x2 v = {lo, hi};
-  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
-}
-
-// max / sum of a value and its copy in lane l^32 (v_permlane32_swap).
-__device__ __forceinline__ float xhalf_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xhalf_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
+constexpr int NW = kFwdWaves;
+constexpr int NT = NW * 64;
 
 // Rescale threshold (log2 units): the running max used for the exponent is
 // only raised when a row's max grows by more than this, so the output
@@ -111,73 +66,97 @@ constexpr float kRescaleLog2 = 8.0f;
 
 template <int DQK, int DV>
 struct Geo {
-  static constexpr int KCH = DQK / 8;                 // 16-byte chunks per K row
-  static constexpr int VCH = DV / 8;                  // 16-byte chunks per V row
-  static constexpr int KSTR = DQK * 2 + 16;           // odd number of 16-byte slots
-  static constexpr int VSTR = DV * 2 + 64;            // 64 mod 256 bytes
-  static constexpr int K_BYTES = BN * KSTR;
-  static constexpr int V_BYTES = BN * VSTR;
+  static constexpr int KPANELS = DQK / 64;               // 64-dim panels of K
+  static constexpr int KPANEL_BYTES = BN * 128;
+  static constexpr int K_BYTES = KPANELS * KPANEL_BYTES;
+  static constexpr int VROWB = DV * 2;                   // 256 (DV=128) or 128 (DV=64)
+  static constexpr int V_BYTES = BN * VROWB;
   static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int NBUF = (2 * STAGE <= 81920) ? 2 : 1;
-  static constexpr int K_LD = (BN * KCH) / NT;        // K chunks per thread
-  static constexpr int V_LD = (BN * VCH) / NT;        // V chunks per thread
-  static constexpr int KK = DQK / 16;                 // MFMA k-steps for S
-  static constexpr int OT = DV / 32;                  // output tiles per wave
-  static_assert((BN * KCH) % NT == 0 && (BN * VCH) % NT == 0, "tile load split");
-  static_assert(((KSTR / 16) & 1) == 1 && (VSTR % 256) == 64 || (DV == 64 && VSTR == 192),
-                "bank spread");
+  static constexpr int K_INST = K_BYTES / 1024;          // wave instructions per K tile
+  static constexpr int V_INST = V_BYTES / 1024;
+  static constexpr int KK = DQK / 16;                    // MFMA k-steps for S
+  static constexpr int OT = DV / 32;                     // output tiles per wave
+  static_assert(K_INST % NW == 0 && V_INST % NW == 0, "tile load split");
+  static_assert(DV == 128 || DV == 64, "V layouts");
 };
 
-template <int DQK, int DV>
-struct Prefetch {
-  u32x4 k[Geo<DQK, DV>::K_LD];
-  u32x4 v[Geo<DQK, DV>::V_LD];
-};
+__device__ __forceinline__ int k_slot(int row, int c) { return c ^ ((row >> 1) & 7); }
 
-template <int DQK, int DV>
-__device__ __forceinline__ void load_tile(Prefetch<DQK, DV>& pf, const __bf16* __restrict__ kb,
-                                          const __bf16* __restrict__ vb, int64_t ks, int64_t vs,
-                                          int key0, int k_last, int tid) {
-  using G = Geo<DQK, DV>;
-#pragma unroll
-  for (int i = 0; i < G::K_LD; ++i) {
-    const int idx = tid + NT * i;
-    const int row = idx / G::KCH, c = idx % G::KCH;
-    const int tok = min(key0 + row, k_last);
-    pf.k[i] = ldg16(kb + (int64_t)tok * ks + c * 8);
-  }
-#pragma unroll
-  for (int i = 0; i < G::V_LD; ++i) {
-    const int idx = tid + NT * i;
-    const int row = idx / G::VCH, c = idx % G::VCH;
-    const int tok = min(key0 + row, k_last);
-    pf.v[i] = ldg16(vb + (int64_t)tok * vs + c * 8);
-  }
+// V chunk slot: 256-byte rows use the dual swizzle; 128-byte rows flip the
+// 64-byte half on alternate row pairs.
+template <int VROWB>
+__device__ __forceinline__ int v_slot(int row, int c) {
+  return VROWB == 256 ? (c ^ swz(row)) : (c ^ (((row >> 1) & 1) << 2));
 }
 
+template <int VROWB>
+__device__ __forceinline__ int v_off(int row, int byte) {
+  return row * VROWB + (v_slot<VROWB>(row, byte >> 4) << 4) + (byte & 15);
+}
+
+__device__ __forceinline__ void g2lds(const void* g, char* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// This wave's share of the direct global->LDS loads of one K/V tile: per
+// instruction a per-lane byte offset (fixed for the whole launch) from the
+// tile's base row, and a wave-uniform LDS destination.
 template <int DQK, int DV>
-__device__ __forceinline__ void store_tile(const Prefetch<DQK, DV>& pf, char* stage, int tid) {
+struct TileLoader {
   using G = Geo<DQK, DV>;
-  char* ks = stage;
-  char* vs = stage + G::K_BYTES;
-#pragma unroll
-  for (int i = 0; i < G::K_LD; ++i) {
-    const int idx = tid + NT * i;
-    const int row = idx / G::KCH, c = idx % G::KCH;
-    *reinterpret_cast<u32x4*>(ks + row * G::KSTR + (c << 4)) = pf.k[i];
+  static constexpr int KI = G::K_INST / NW, VI = G::V_INST / NW;
+  static constexpr int VCH = G::VROWB / 16, RPI = 1024 / G::VROWB;
+  uint32_t koff[KI], voff[VI];  // byte offsets from the tile's first key row
+  int wave, lane;
+
+  __device__ __forceinline__ int krow(int jj) const { return ((wave + NW * jj) % (BN / 8)) * 8 + (lane >> 3); }
+  __device__ __forceinline__ int kcol(int jj) const {
+    return ((wave + NW * jj) / (BN / 8) * 64 + k_slot(krow(jj), lane & 7) * 8) * 2;  // XOR involution
   }
-#pragma unroll
-  for (int i = 0; i < G::V_LD; ++i) {
-    const int idx = tid + NT * i;
-    const int row = idx / G::VCH, c = idx % G::VCH;
-    *reinterpret_cast<u32x4*>(vs + row * G::VSTR + (c << 4)) = pf.v[i];
+  __device__ __forceinline__ int kdst(int jj) const {
+    const int j = wave + NW * jj;
+    return j / (BN / 8) * G::KPANEL_BYTES + (j % (BN / 8)) * 1024;
   }
+  __device__ __forceinline__ int vrow(int jj) const { return (wave + NW * jj) * RPI + lane / VCH; }
+  __device__ __forceinline__ int vcol(int jj) const { return v_slot<G::VROWB>(vrow(jj), lane % VCH) * 16; }
+  __device__ __forceinline__ int vdst(int jj) const { return G::K_BYTES + (wave + NW * jj) * 1024; }
+
+  __device__ __forceinline__ void init(int64_t ks_bytes, int64_t vs_bytes, int w, int l) {
+    wave = w;
+    lane = l;
+#pragma unroll
+    for (int jj = 0; jj < KI; ++jj) koff[jj] = (uint32_t)(krow(jj) * ks_bytes + kcol(jj));
+#pragma unroll
+    for (int jj = 0; jj < VI; ++jj) voff[jj] = (uint32_t)(vrow(jj) * vs_bytes + vcol(jj));
+  }
+
+  // rows_left: key rows available from the tile's first row on (clamp the last tile only)
+  __device__ __forceinline__ void issue(const char* kt, const char* vt, int64_t ks_bytes,
+                                        int64_t vs_bytes, int rows_left, char* stage) const {
+    if (rows_left >= BN) {
+#pragma unroll
+      for (int jj = 0; jj < KI; ++jj) g2lds(kt + koff[jj], stage + kdst(jj));
+#pragma unroll
+      for (int jj = 0; jj < VI; ++jj) g2lds(vt + voff[jj], stage + vdst(jj));
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < KI; ++jj)
+        g2lds(kt + min(krow(jj), rows_left - 1) * ks_bytes + kcol(jj), stage + kdst(jj));
+#pragma unroll
+      for (int jj = 0; jj < VI; ++jj)
+        g2lds(vt + min(vrow(jj), rows_left - 1) * vs_bytes + vcol(jj), stage + vdst(jj));
+    }
+  }
+};
+
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return __builtin_fmaxf(a, __builtin_fmaxf(b, c));
 }
 
 template <int DQK, int DV, bool CAUSAL, bool MERGE>
 __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   using G = Geo<DQK, DV>;
-  __shared__ __attribute__((aligned(16))) char smem[G::NBUF * G::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * G::STAGE];
 
   const int nb = gridDim.x;
   int b = xcd_remap(blockIdx.x, nb);
@@ -200,7 +179,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   if (klen <= 0 && MERGE) return;  // merging an empty block is the identity
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep it scalar
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int g = lane >> 5;
@@ -211,17 +190,23 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   const int ntiles = (kend + BN - 1) / BN;
 
   // this wave's rows
-  const int wq0 = q0 + wave * kFwdRowsPerWave;        // first row of the wave
+  const int wq0 = q0 + wave * kFwdRowsPerWave;
   const bool wave_live = wq0 < q_hi;
   const int wq_first_rel = wq0 - q_lo;
   const int wq_last_rel = min(wq0 + kFwdRowsPerWave, q_hi) - 1 - q_lo;
   const int wave_kend = CAUSAL ? min(klen, wq_last_rel + 1) : klen;
-  const int my_row = wq0 + l32;                        // query token of this lane
+  const int my_row = wq0 + l32;
   const int my_row_rel = my_row - q_lo;
 
   const __bf16* __restrict__ qb = reinterpret_cast<const __bf16*>(a.q) + (int64_t)h * DQK;
-  const __bf16* __restrict__ kb = reinterpret_cast<const __bf16*>(a.k) + (int64_t)kvh * DQK;
-  const __bf16* __restrict__ vb = reinterpret_cast<const __bf16*>(a.v) + (int64_t)kvh * DV;
+  const int64_t ks_bytes = a.k_stride * 2, vs_bytes = a.v_stride * 2;
+  const char* kbase = reinterpret_cast<const char*>(a.k) + ((int64_t)k_lo * a.k_stride + (int64_t)kvh * DQK) * 2;
+  const char* vbase = reinterpret_cast<const char*>(a.v) + ((int64_t)k_lo * a.v_stride + (int64_t)kvh * DV) * 2;
+
+  TileLoader<DQK, DV> ld;
+  ld.init(ks_bytes, vs_bytes, wave, lane);
+  // the first K/V tile streams in while Q is fetched
+  if (ntiles > 0) ld.issue(kbase, vbase, ks_bytes, vs_bytes, klen, smem);
 
   // Q^T operand: lane holds row my_row, dims 16*kk + 8*g .. +7
   bf16x8 qf[G::KK];
@@ -234,31 +219,34 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 
   f32x16 o[G::OT];
 #pragma unroll
-  for (int t = 0; t < G::OT; ++t)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
-  float m_run = -INFINITY;  // running max of raw scores
+  for (int t = 0; t < G::OT; ++t) o[t] = zero16();
+  float m_run = -INFINITY;  // running max of raw scores (possibly stale, see above)
   float l_run = 0.f;        // running sum of this lane's 16-key halves
   const float c2 = a.scale_log2;
 
-  const int k_last = k_hi - 1;
-  const int krow_a = sigma(l32);
-  // transposing-read address of this lane: key row 8g + (lane%16)/4, dims
-  // 16*((lane/16)%2) + 4*(lane%4) (+32 per output tile, +4 rows for keys 4..7)
-  const int v_row = 8 * g + ((lane & 15) >> 2);
-  const int v_col = (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-
-  Prefetch<DQK, DV> pf;
-  if (ntiles > 0) {
-    load_tile<DQK, DV>(pf, kb, vb, a.k_stride, a.v_stride, k_lo, k_last, tid);
-    store_tile<DQK, DV>(pf, smem, tid);
-    if (ntiles > 1)
-      load_tile<DQK, DV>(pf, kb, vb, a.k_stride, a.v_stride, k_lo + BN, k_last, tid);
+  // per-lane LDS read offsets; K rows +32 and V rows +16 keep the swizzle
+  int koff[4];
+  {
+    const int r = sigma(l32);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) koff[q] = r * 128 + (k_slot(r, 2 * q + g) << 4);
   }
+  int voff[2][G::OT];
+  {
+    const int trr = tr_row(lane), trc = tr_col_bytes(lane);
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int tt = 0; tt < G::OT; ++tt) voff[h2][tt] = v_off<G::VROWB>(trr + 4 * h2, 64 * tt + trc);
+  }
+
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const char* stage = smem + (G::NBUF == 2 ? (t & 1) * G::STAGE : 0);
+  auto tile = [&](const int t, char* const stage, char* const next) __attribute__((always_inline)) {
+    if (t + 1 < ntiles)
+      ld.issue(kbase + (int64_t)(t + 1) * BN * ks_bytes, vbase + (int64_t)(t + 1) * BN * vs_bytes,
+               ks_bytes, vs_bytes, klen - (t + 1) * BN, next);
     const int kt0 = t * BN;  // relative to k_lo
     if (wave_live && kt0 < wave_kend) {
       const char* ks = stage;
@@ -267,13 +255,11 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
       f32x16 s[2];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[hh][i] = 0.f;
-        const char* rp = ks + (krow_a + 32 * hh) * G::KSTR + (g << 4);
+        s[hh] = zero16();
 #pragma unroll
         for (int kk = 0; kk < G::KK; ++kk) {
-          const u32x4 kv = *reinterpret_cast<const u32x4*>(rp + (kk << 5));
-          s[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qf[kk], s[hh], 0, 0, 0);
+          const u32x4 kv = lds16(ks + koff[kk & 3] + (kk >> 2) * G::KPANEL_BYTES + hh * 32 * 128);
+          s[hh] = mma(as_bf16x8(kv), qf[kk], s[hh]);
         }
       }
       // ---- mask (only tiles that cross the causal diagonal or the part end)
@@ -289,14 +275,15 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
           }
       }
       // ---- online softmax (log2 domain, lazily rescaled)
-      float mx = fmaxf(s[0][0], s[0][1]);
+      float mx = max3f(s[0][0], s[0][1], s[0][2]);
 #pragma unroll
-      for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[0][i], s[0][i + 1]));
+      for (int i = 3; i < 15; i += 2) mx = max3f(mx, s[0][i], s[0][i + 1]);
+      mx = max3f(mx, s[0][15], s[1][0]);
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[1][i], s[1][i + 1]));
+      for (int i = 1; i < 15; i += 2) mx = max3f(mx, s[1][i], s[1][i + 1]);
+      mx = fmaxf(mx, s[1][15]);
       mx = xhalf_max(mx);
-      // raise the running max only if it grew by more than the threshold
-      const bool raise = (mx - m_run) * c2 > kRescaleLog2;   // true on the first live tile
+      const bool raise = (mx - m_run) * c2 > kRescaleLog2;  // true on the first live tile
       if (__builtin_amdgcn_ballot_w64(raise)) {
         const float m_new = raise ? mx : m_run;
         const float m_use_new = (m_new == -INFINITY) ? 0.f : m_new;
@@ -309,47 +296,35 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
           for (int i = 0; i < 16; ++i) o[tt][i] *= alpha;
       }
       const float mc = ((m_run == -INFINITY) ? 0.f : m_run) * c2;
-      float rs = 0.f;
-      unsigned pk[16];
+      float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[hh][i], c2, -mc));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[hh][i + 1], c2, -mc));
-          rs += p0 + p1;
-          pk[hh * 8 + (i >> 1)] = pack_bf16x2(p0, p1);
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[hh][i], c2, -mc));
+          if (i & 1) rs1 += p; else rs0 += p;
+          s[hh][i] = p;
         }
-      l_run += rs;
+      l_run += rs0 + rs1;
       // ---- O^T += V^T * P^T : 4 k-steps of 16 keys
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
-        u32x4 pv;
-        pv[0] = pk[4 * bb + 0];
-        pv[1] = pk[4 * bb + 1];
-        pv[2] = pk[4 * bb + 2];
-        pv[3] = pk[4 * bb + 3];
-        const bf16x8 pb = as_bf16x8(pv);
-        // V^T operand: keys 16bb + 8g + 0..7 of dim 32tt + l32, two transposing reads
-        const char* vp = vsm + (16 * bb + v_row) * G::VSTR + v_col;
+        const bf16x8 pb = pack8(s[bb >> 1], 8 * (bb & 1));
 #pragma unroll
         for (int tt = 0; tt < G::OT; ++tt) {
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 64 * tt));
-          const s16x4 hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 4 * G::VSTR + 64 * tt));
-          const bf16x8 va = __builtin_bit_cast(
-              bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[tt], 0, 0, 0);
+          const char* vp = vsm + bb * 16 * G::VROWB;
+          const bf16x8 va = cat_tr(lds_tr(vp + voff[0][tt]), lds_tr(vp + voff[1][tt]));
+          o[tt] = mma(va, pb, o[tt]);
         }
       }
     }
-    if (t + 1 < ntiles) {
-      if (G::NBUF == 1) __syncthreads();
-      store_tile<DQK, DV>(pf, smem + (G::NBUF == 2 ? ((t + 1) & 1) * G::STAGE : 0), tid);
-      __syncthreads();
-      if (t + 2 < ntiles)
-        load_tile<DQK, DV>(pf, kb, vb, a.k_stride, a.v_stride, k_lo + (t + 2) * BN, k_last, tid);
-    }
+    // next tile landed (own loads) and every wave is done with this one
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(t, smem, smem + G::STAGE);
+    if (t + 1 < ntiles) tile(t + 1, smem + G::STAGE, smem);
   }
 
   if (!wave_live || my_row >= q_hi) return;
@@ -359,7 +334,8 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   const bool empty = !(l_tot > 0.f);
   const float inv = empty ? 0.f : 1.f / l_tot;
   const float m_fin = (m_run == -INFINITY) ? 0.f : m_run;
-  const float lse = empty ? -INFINITY : (m_fin * a.scale + __builtin_amdgcn_logf(l_tot) * 0.69314718055994531f);
+  const float lse =
+      empty ? -INFINITY : (m_fin * a.scale + __builtin_amdgcn_logf(l_tot) * 0.69314718055994531f);
 
   float* orow = a.out + ((int64_t)my_row * a.hq + h) * DV;
   float* lrow = a.lse + (int64_t)h * a.total_q + my_row;
