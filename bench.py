@@ -42,6 +42,9 @@ def parse():
                     help="1: merge in the attention epilogue instead of ra_lse_merge")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the oracle CPU baseline sample (0 = skip)")
+    ap.add_argument("--backward", type=int, default=0,
+                    help="1: time the backward shares (after one forward) instead; for the "
+                         "256K MLA workload")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB 3 times (the "
                          "reference kernel that scales HBM byte counters), then exit")
@@ -116,6 +119,76 @@ def cpu_baseline(w, budget_s: float):
                       f"{w.hq} query heads over every visible key, float64 NumPy, {dt:.1f} s"}
 
 
+def bench_backward(a, w, prob, torch, L):
+    """Backward step: every rank's ra_rank_backward (delta, then dQ and dK/dV per block)."""
+    import synth
+    C = w.cp
+    dev = prob.q[0].device
+    do = synth.cast(w.do(), w.dtype).to(dev)
+    prob.do = [prob.gather(do, r) for r in range(C)]
+    del do
+    fwd = []
+    for r in range(C):
+        out, lse, ws = prob.alloc_forward(torch.bfloat16, True)
+        prob.forward(r, out, lse, ws, fuse_merge=True)
+        fwd.append((out, lse))
+    del ws
+    dqs = [torch.zeros((prob.Tl, prob.hq, prob.dqk), device=dev) for _ in range(C)]
+    dks = [torch.zeros((prob.Tl, prob.hkv, prob.dqk), device=dev) for _ in range(C)]
+    dvs = [torch.zeros((prob.Tl, prob.hkv, prob.dv), device=dev) for _ in range(C)]
+    n = L.ra_rank_backward_workspace(prob.backward_desc(0, fwd[0][0], fwd[0][1], dqs[0], dks,
+                                                        dvs, None))
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    work = [prob.work(r) for r in range(C)]
+    fl_pair = 2 * (3 * w.dqk + 2 * w.dv)
+    step_flops = sum(p for r in range(C) for (p, _, _) in work[r]) * fl_pair
+    stream = torch.cuda.current_stream()
+
+    def run_step(events=None):
+        for r in range(C):
+            prob.backward(r, fwd[r][0], fwd[r][1], dqs[r], dks, dvs, ws,
+                          events=None if events is None else events[r])
+
+    for _ in range(a.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2 * C)] for _ in range(C)]
+          for _ in range(a.steps)]
+    for e3 in ev:
+        for e2 in e3:
+            for e in e2:
+                e.record(stream)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(a.steps):
+        run_step(ev[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / a.steps
+    blk_ms = sum(ev[i][r][2 * s].elapsed_time(ev[i][r][2 * s + 1])
+                 for i in range(a.steps) for r in range(C) for s in range(C))
+    achieved = step_flops * a.steps / (blk_ms / 1e3) / 1e12
+    res = {
+        "metric": "effective attention backward TFLOP/s per rank-share (bf16), 1 GPU",
+        "value": round(step_flops / (ms_step / 1e3) / 1e12, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), bf16 RNE)",
+        "config": {"workload": f"{w.name}: backward of all {C} rank shares (dQ, dK, dV "
+                               f"recomputed from the saved lse), S={w.seqlen}, {w.hq} heads, "
+                               f"head dim {w.dqk}/{w.dv}",
+                   "step_effective_tflop": round(step_flops / 1e12, 4),
+                   "flop_per_pair": fl_pair},
+        "roofline": {"bound": "mfma", "kernel": "attn_bwd_dq + attn_bwd_dkdv",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -145,6 +218,8 @@ def main():
     torch.cuda.empty_cache()
 
     C = w.cp
+    if a.backward:
+        return bench_backward(a, w, prob, torch, L)
     bufs = [prob.alloc_forward(torch.bfloat16, bool(a.fuse_merge)) for _ in range(C)]
     work = [prob.work(r) for r in range(C)]                      # per step (pairs*hq, ...)
     fl_pair = 2 * (w.dqk + w.dv)
