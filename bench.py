@@ -4,7 +4,10 @@
 A step is one pass of the whole forward hot path over one batch of the
 workload: for every simulated rank r of the CP group, ``ra_rank_forward``
 (the diagonal causal block, the C-1 history blocks, the lse merges and the
-bf16 finalisation) on the rank's zig-zag shard, all on one stream.
+bf16 finalisation) on the rank's zig-zag shard, all on one stream.  By
+default (``--fuse-merge 2``) each rank share is one launch that walks every
+block with the online-softmax state in registers; ``--fuse-merge 0`` runs
+one launch per block plus ``ra_lse_merge`` per history block.
 
 Default workload: 32K grouped-query causal attention (32 query heads over
 8 KV heads, head dim 128, bf16), zig-zag CP=8, N(0,1)*0.5 inputs.
@@ -38,8 +41,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gqa_32k")
-    ap.add_argument("--fuse-merge", type=int, default=0,
-                    help="1: merge in the attention epilogue instead of ra_lse_merge")
+    ap.add_argument("--fuse-merge", type=int, default=2,
+                    help="0: per-step partials + ra_lse_merge; 1: merge in the attention "
+                         "epilogue; 2: the whole rank share in one launch")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the oracle CPU baseline sample (0 = skip)")
     ap.add_argument("--backward", type=int, default=0,
@@ -220,7 +224,7 @@ def main():
     C = w.cp
     if a.backward:
         return bench_backward(a, w, prob, torch, L)
-    bufs = [prob.alloc_forward(torch.bfloat16, bool(a.fuse_merge)) for _ in range(C)]
+    bufs = [prob.alloc_forward(torch.bfloat16, a.fuse_merge) for _ in range(C)]
     work = [prob.work(r) for r in range(C)]                      # per step (pairs*hq, ...)
     fl_pair = 2 * (w.dqk + w.dv)
     step_flops = sum(p for r in range(C) for (p, _, _) in work[r]) * fl_pair
@@ -235,7 +239,7 @@ def main():
     def run_step(events=None):
         for r in range(C):
             out, lse, ws = bufs[r]
-            prob.forward(r, out, lse, ws, fuse_merge=bool(a.fuse_merge),
+            prob.forward(r, out, lse, ws, fuse_merge=a.fuse_merge,
                          events=None if events is None else events[r])
 
     for _ in range(a.warmup):
@@ -266,6 +270,12 @@ def main():
     n_launch = 0
     for i in range(a.steps):
         for r in range(C):
+            if a.fuse_merge == 2:                                # one launch per rank share
+                d = ev[i][r][0].elapsed_time(ev[i][r][1])
+                attn_ms += d
+                attn_flops += sum(p for (p, _, _) in work[r]) * fl_pair
+                n_launch += 1
+                continue
             for s in range(C):
                 d = ev[i][r][2 * s].elapsed_time(ev[i][r][2 * s + 1])
                 f = work[r][s][0] * fl_pair
@@ -302,12 +312,12 @@ def main():
                         f"(all {w.cp} rank shares forward, one after another), "
                         f"{w.hq} q heads / {w.hkv} kv heads, head dim {w.dqk}/{w.dv}",
             "seq_len": w.seqlen, "cp": w.cp, "hq": w.hq, "hkv": w.hkv, "dqk": w.dqk,
-            "dv": w.dv, "fuse_merge": bool(a.fuse_merge),
+            "dv": w.dv, "fuse_merge": a.fuse_merge,
             "step_effective_tflop": round(step_flops / 1e12, 4),
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_fwd_bf16",
+            "kernel": "attn_fwd_bf16" + (" (whole rank share per launch)" if a.fuse_merge == 2 else ""),
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

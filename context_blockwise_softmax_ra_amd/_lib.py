@@ -220,7 +220,7 @@ def rank_desc(local: AttnDesc, cp_size: int, rank: int, k_blocks: Sequence, v_bl
     r.lse = _ptr(lse)
     r.workspace = _ptr(workspace) if workspace is not None else None
     r.workspace_bytes = (workspace.numel() * workspace.element_size()) if workspace is not None else 0
-    r.fuse_merge = 1 if fuse_merge else 0
+    r.fuse_merge = int(fuse_merge)
     ev = None
     if events is not None:
         ev = (c_void_p * len(events))(*[e if isinstance(e, int) else (e.cuda_event if e is not None else None)

@@ -382,6 +382,10 @@ ra_status ra_rank_forward_workspace(const ra_rank_desc* d, size_t* bytes) {
   const size_t out_b = align256((size_t)c.total_q * d->local.hq * d->local.dv * sizeof(float));
   const size_t lse_b = align256((size_t)c.total_q * d->local.hq * sizeof(float));
   size_t b = 0;
+  if (d->fuse_merge == 2 && d->local.dtype == RA_BF16) {
+    *bytes = 0;  // one launch, output written directly
+    return ok();
+  }
   if (d->out_dtype != RA_FP32) b += out_b;                   // fp32 accumulator
   if (!d->fuse_merge && d->cp_size > 1) b += out_b + lse_b;  // one partial
   *bytes = b;
@@ -406,6 +410,43 @@ ra_status ra_rank_forward(const ra_rank_desc* d, void* stream) {
   if (need && !aligned16(d->workspace))
     return fail(RA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   const ra_attn_desc& L = d->local;
+  hipError_t e;
+  if (d->fuse_merge == 2 && L.dtype == RA_BF16) {
+    // the whole share in one launch: every owner's block in ring order,
+    // merged in registers, final output written by the epilogue
+    if (d->cp_size > ra::kMaxCp)
+      return fail(RA_ERR_UNSUPPORTED, "fused rank forward supports cp_size <= %d", ra::kMaxCp);
+    ra::RankKV rk;
+    std::memset(&rk, 0, sizeof(rk));
+    rk.cp = d->cp_size;
+    rk.rank = d->rank;
+    for (int j = 0; j < d->cp_size; ++j) {
+      rk.k[j] = d->k_blocks[j];
+      rk.v[j] = d->v_blocks[j];
+    }
+    ra_attn_desc sd = L;
+    sd.k = d->k_blocks[0];
+    sd.v = d->v_blocks[0];
+    sd.causal = 1;
+    sd.q_part = RA_PART_ALL;
+    sd.k_part = RA_PART_ALL;
+    Checked cs;
+    if ((st = check_desc(&sd, true, &cs)) != RA_OK) return st;
+    ra::AttnArgs a = make_args(&sd, cs);
+    a.out = static_cast<float*>(d->out);
+    a.lse = d->lse;
+    if (d->events && d->events[0] &&
+        (e = hipEventRecord((hipEvent_t)d->events[0], hs)) != hipSuccess)
+      return hip_fail(e, "event record");
+    if (a.n_qtiles > 0) {
+      e = ra::launch_rank_fwd_bf16(a, rk, L.dqk, L.dv, d->out_dtype == RA_BF16, hs);
+      if (e != hipSuccess) return hip_fail(e, "rank forward launch");
+    }
+    if (d->events && d->events[1] &&
+        (e = hipEventRecord((hipEvent_t)d->events[1], hs)) != hipSuccess)
+      return hip_fail(e, "event record");
+    return ok();
+  }
   const size_t out_b = align256((size_t)c.total_q * L.hq * L.dv * sizeof(float));
   char* ws = static_cast<char*>(d->workspace);
   float* acc = nullptr;
@@ -422,7 +463,6 @@ ra_status ra_rank_forward(const ra_rank_desc* d, void* stream) {
     ws += out_b;
     part_lse = reinterpret_cast<float*>(ws);
   }
-  hipError_t e;
   for (int s = 0; s < d->cp_size; ++s) {
     const Step p = plan_step(d->rank, s, d->cp_size);
     ra_attn_desc sd = L;

@@ -153,8 +153,26 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return __builtin_fmaxf(a, __builtin_fmaxf(b, c));
 }
 
-template <int DQK, int DV, bool CAUSAL, bool MERGE>
-__global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
+// How a KV block meets the rows of a workgroup.
+enum BlockKind {
+  KIND_CAUSAL = 0,     // key j visible to row i iff j <= i (part-relative)
+  KIND_ALL = 1,        // every key visible
+  KIND_LATE_ROWS = 2,  // every key visible to rows of the segment's second half only
+};
+
+struct Block {
+  const char* kb;  // K of the block's first key (this kv head)
+  const char* vb;
+  int klen;
+  int kind;
+  int ntiles;
+};
+
+// MODE: 0 = one non-causal block, 1 = one causal block (both as described by
+// the AttnArgs parts), 2 = a rank's whole share: the C blocks of RankKV in
+// ring order, merged in registers (no partials, no separate merge).
+template <int DQK, int DV, int MODE, bool MERGE, bool OUT_BF16>
+__global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV rk) {
   using G = Geo<DQK, DV>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * G::STAGE];
 
@@ -167,16 +185,16 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   b /= a.n_qtiles;
   const int kvh = b % a.hkv;
   const int seg = b / a.hkv;
-  const int qt = CAUSAL ? (a.n_qtiles - 1 - qt_rev) : qt_rev;
+  // heaviest query tiles first (causal: later rows see more keys; rank share:
+  // second-half rows also see the blocks of later ranks)
+  const int qt = MODE != 0 ? (a.n_qtiles - 1 - qt_rev) : qt_rev;
   const int h = kvh * group + hg;
 
-  int q_lo, q_hi, k_lo, k_hi;
-  part_range(a.cu_q[seg], a.cu_q[seg + 1], a.q_part, &q_lo, &q_hi);
-  part_range(a.cu_k[seg], a.cu_k[seg + 1], a.k_part, &k_lo, &k_hi);
+  int q_lo, q_hi;
+  part_range(a.cu_q[seg], a.cu_q[seg + 1], MODE == 2 ? RA_PART_ALL : a.q_part, &q_lo, &q_hi);
   const int q0 = q_lo + qt * BM;
   if (q0 >= q_hi) return;
-  const int klen = k_hi - k_lo;
-  if (klen <= 0 && MERGE) return;  // merging an empty block is the identity
+  const int qhalf = (q_hi - q_lo) >> 1;  // second-half rows start here (part-relative)
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep it scalar
@@ -184,33 +202,89 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
-  // key range of the whole workgroup
   const int qrel_last_wg = min(q0 + BM, q_hi) - 1 - q_lo;
-  const int kend = CAUSAL ? min(klen, qrel_last_wg + 1) : klen;
-  const int ntiles = (kend + BN - 1) / BN;
-
-  // this wave's rows
   const int wq0 = q0 + wave * kFwdRowsPerWave;
   const bool wave_live = wq0 < q_hi;
   const int wq_first_rel = wq0 - q_lo;
   const int wq_last_rel = min(wq0 + kFwdRowsPerWave, q_hi) - 1 - q_lo;
-  const int wave_kend = CAUSAL ? min(klen, wq_last_rel + 1) : klen;
   const int my_row = wq0 + l32;
   const int my_row_rel = my_row - q_lo;
-
-  const __bf16* __restrict__ qb = reinterpret_cast<const __bf16*>(a.q) + (int64_t)h * DQK;
   const int64_t ks_bytes = a.k_stride * 2, vs_bytes = a.v_stride * 2;
-  const char* kbase = reinterpret_cast<const char*>(a.k) + ((int64_t)k_lo * a.k_stride + (int64_t)kvh * DQK) * 2;
-  const char* vbase = reinterpret_cast<const char*>(a.v) + ((int64_t)k_lo * a.v_stride + (int64_t)kvh * DV) * 2;
+  const int nblocks = MODE == 2 ? rk.cp : 1;
+
+  // block bi of this workgroup, with the number of key tiles it visits
+  auto get_block = [&](int bi) -> Block {
+    Block blk;
+    const void* kp;
+    const void* vp;
+    int kpart;
+    if (MODE == 2) {
+      const int owner = (rk.rank - bi + rk.cp) % rk.cp;
+      kp = rk.k[owner];
+      vp = rk.v[owner];
+      // diagonal: causal; earlier owners: all rows x their first half;
+      // later owners: second-half rows x all their keys
+      blk.kind = bi == 0 ? KIND_CAUSAL : (owner < rk.rank ? KIND_ALL : KIND_LATE_ROWS);
+      kpart = (bi != 0 && owner < rk.rank) ? RA_PART_FIRST_HALF : RA_PART_ALL;
+    } else {
+      kp = a.k;
+      vp = a.v;
+      blk.kind = MODE == 1 ? KIND_CAUSAL : KIND_ALL;
+      kpart = a.k_part;
+    }
+    int k_lo, k_hi;
+    part_range(a.cu_k[seg], a.cu_k[seg + 1], kpart, &k_lo, &k_hi);
+    blk.klen = k_hi - k_lo;
+    blk.kb = reinterpret_cast<const char*>(kp) + ((int64_t)k_lo * a.k_stride + (int64_t)kvh * DQK) * 2;
+    blk.vb = reinterpret_cast<const char*>(vp) + ((int64_t)k_lo * a.v_stride + (int64_t)kvh * DV) * 2;
+    int kend = blk.klen;
+    if (blk.kind == KIND_CAUSAL) kend = min(blk.klen, qrel_last_wg + 1);
+    if (blk.kind == KIND_LATE_ROWS && qrel_last_wg < qhalf) kend = 0;
+    blk.ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+    return blk;
+  };
+
+  // cursors over the (block, tile) sequence: one for loads, one tile ahead
+  // of the one for compute
+  struct Cursor {
+    int bi, t;
+    Block blk;
+  };
+  auto first = [&](Cursor& c) {
+    c.bi = 0;
+    c.t = 0;
+    c.blk = get_block(0);
+    while (c.blk.ntiles == 0 && c.bi + 1 < nblocks) c.blk = get_block(++c.bi);
+  };
+  auto advance = [&](Cursor& c) {
+    if (++c.t < c.blk.ntiles) return;
+    c.t = 0;
+    do {
+      if (++c.bi >= nblocks) return;
+      c.blk = get_block(c.bi);
+    } while (c.blk.ntiles == 0);
+  };
+  int total = 0;
+  for (int bi = 0; bi < nblocks; ++bi) total += get_block(bi).ntiles;
+  if (total == 0 && MERGE) return;  // merging an empty block is the identity
 
   TileLoader<DQK, DV> ld;
   ld.init(ks_bytes, vs_bytes, wave, lane);
+  Cursor lc, cc;
+  first(lc);
+  cc = lc;
+  auto issue_next = [&](char* stage) {
+    ld.issue(lc.blk.kb + (int64_t)lc.t * BN * ks_bytes, lc.blk.vb + (int64_t)lc.t * BN * vs_bytes,
+             ks_bytes, vs_bytes, lc.blk.klen - lc.t * BN, stage);
+    advance(lc);
+  };
   // the first K/V tile streams in while Q is fetched
-  if (ntiles > 0) ld.issue(kbase, vbase, ks_bytes, vs_bytes, klen, smem);
+  if (total > 0) issue_next(smem);
 
   // Q^T operand: lane holds row my_row, dims 16*kk + 8*g .. +7
   bf16x8 qf[G::KK];
   {
+    const __bf16* qb = reinterpret_cast<const __bf16*>(a.q) + (int64_t)h * DQK;
     const int row = min(my_row, q_hi - 1);
     const __bf16* qp = qb + (int64_t)row * a.q_stride + 8 * g;
 #pragma unroll
@@ -243,12 +317,22 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  auto tile = [&](const int t, char* const stage, char* const next) __attribute__((always_inline)) {
-    if (t + 1 < ntiles)
-      ld.issue(kbase + (int64_t)(t + 1) * BN * ks_bytes, vbase + (int64_t)(t + 1) * BN * vs_bytes,
-               ks_bytes, vs_bytes, klen - (t + 1) * BN, next);
-    const int kt0 = t * BN;  // relative to k_lo
-    if (wave_live && kt0 < wave_kend) {
+  auto tile = [&](const int gi, char* const stage, char* const next) __attribute__((always_inline)) {
+    if (gi + 1 < total) issue_next(next);
+    const int kt0 = cc.t * BN;  // relative to the block's first key
+    const int klen = cc.blk.klen, kind = cc.blk.kind;
+    // rows of this wave the tile can reach, and whether scores need a mask
+    bool live = wave_live, need_mask;
+    if (kind == KIND_CAUSAL) {
+      live = live && kt0 <= wq_last_rel;
+      need_mask = (kt0 + BN > klen) || (kt0 + BN - 1 > wq_first_rel);
+    } else if (kind == KIND_LATE_ROWS) {
+      live = live && wq_last_rel >= qhalf;
+      need_mask = (kt0 + BN > klen) || (wq_first_rel < qhalf);
+    } else {
+      need_mask = kt0 + BN > klen;
+    }
+    if (live) {
       const char* ks = stage;
       const char* vsm = stage + G::K_BYTES;
       // ---- S^T = K * Q^T : two 32-key halves
@@ -262,15 +346,16 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
           s[hh] = mma(as_bf16x8(kv), qf[kk], s[hh]);
         }
       }
-      // ---- mask (only tiles that cross the causal diagonal or the part end)
-      const bool need_mask = (kt0 + BN > wave_kend) || (CAUSAL && kt0 + BN - 1 > wq_first_rel);
+      // ---- mask (tiles crossing the causal diagonal, a part end, or the
+      // segment's half for second-half-only blocks)
       if (need_mask) {
+        const bool row_ok = kind != KIND_LATE_ROWS || my_row_rel >= qhalf;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int kr = kt0 + 32 * hh + ((i >> 3) << 4) + (g << 3) + (i & 7);
-            const bool ok = (kr < klen) && (!CAUSAL || kr <= my_row_rel);
+            const bool ok = row_ok && (kr < klen) && (kind != KIND_CAUSAL || kr <= my_row_rel);
             if (!ok) s[hh][i] = -INFINITY;
           }
       }
@@ -318,13 +403,14 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
         }
       }
     }
+    advance(cc);
     // next tile landed (own loads) and every wave is done with this one
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  for (int t = 0; t < ntiles; t += 2) {
-    tile(t, smem, smem + G::STAGE);
-    if (t + 1 < ntiles) tile(t + 1, smem + G::STAGE, smem);
+  for (int gi = 0; gi < total; gi += 2) {
+    tile(gi, smem, smem + G::STAGE);
+    if (gi + 1 < total) tile(gi + 1, smem + G::STAGE, smem);
   }
 
   if (!wave_live || my_row >= q_hi) return;
@@ -337,9 +423,22 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   const float lse =
       empty ? -INFINITY : (m_fin * a.scale + __builtin_amdgcn_logf(l_tot) * 0.69314718055994531f);
 
-  float* orow = a.out + ((int64_t)my_row * a.hq + h) * DV;
   float* lrow = a.lse + (int64_t)h * a.total_q + my_row;
-  if (!MERGE) {
+  if (OUT_BF16) {
+    // final output straight to bf16 (round to nearest even)
+    unsigned short* orow = reinterpret_cast<unsigned short*>(a.out) + ((int64_t)my_row * a.hq + h) * DV;
+#pragma unroll
+    for (int tt = 0; tt < G::OT; ++tt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        uint2 w;
+        w.x = pack_bf16x2(o[tt][4 * q4 + 0] * inv, o[tt][4 * q4 + 1] * inv);
+        w.y = pack_bf16x2(o[tt][4 * q4 + 2] * inv, o[tt][4 * q4 + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + 32 * tt + 8 * q4 + 4 * g) = w;
+      }
+    if (g == 0) *lrow = lse;
+  } else if (!MERGE) {
+    float* orow = a.out + ((int64_t)my_row * a.hq + h) * DV;
 #pragma unroll
     for (int tt = 0; tt < G::OT; ++tt)
 #pragma unroll
@@ -353,6 +452,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
       }
     if (g == 0) *lrow = lse;
   } else {
+    float* orow = a.out + ((int64_t)my_row * a.hq + h) * DV;
     const float la = *lrow;
     const float mm = fmaxf(la, lse);
     const bool both_empty = (mm == -INFINITY);
@@ -379,17 +479,26 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 }
 
 template <int DQK, int DV>
-hipError_t launch_t(const AttnArgs& a, bool causal, bool merge, hipStream_t st) {
+hipError_t launch_t(const AttnArgs& a, const RankKV* rk, bool causal, bool merge, bool out_bf16,
+                    hipStream_t st) {
   const long long nblk = (long long)a.n_seq * a.hkv * a.n_qtiles * a.group;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)nblk), block(NT);
-  if (causal) {
-    if (merge) hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, true, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, true, false>), grid, block, 0, st, a);
+  RankKV none;
+  none.cp = 0;
+  none.rank = 0;
+  if (rk) {
+    if (out_bf16)
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, 2, false, true>), grid, block, 0, st, a, *rk);
+    else
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, 2, false, false>), grid, block, 0, st, a, *rk);
+  } else if (causal) {
+    if (merge) hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, 1, true, false>), grid, block, 0, st, a, none);
+    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, 1, false, false>), grid, block, 0, st, a, none);
   } else {
-    if (merge) hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, false, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, false, false>), grid, block, 0, st, a);
+    if (merge) hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, 0, true, false>), grid, block, 0, st, a, none);
+    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, 0, false, false>), grid, block, 0, st, a, none);
   }
   return hipGetLastError();
 }
@@ -398,9 +507,17 @@ hipError_t launch_t(const AttnArgs& a, bool causal, bool merge, hipStream_t st) 
 
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int dqk, int dv, bool causal, bool merge,
                                 hipStream_t st) {
-  if (dqk == 128 && dv == 128) return launch_t<128, 128>(a, causal, merge, st);
-  if (dqk == 192 && dv == 128) return launch_t<192, 128>(a, causal, merge, st);
-  if (dqk == 64 && dv == 64) return launch_t<64, 64>(a, causal, merge, st);
+  if (dqk == 128 && dv == 128) return launch_t<128, 128>(a, nullptr, causal, merge, false, st);
+  if (dqk == 192 && dv == 128) return launch_t<192, 128>(a, nullptr, causal, merge, false, st);
+  if (dqk == 64 && dv == 64) return launch_t<64, 64>(a, nullptr, causal, merge, false, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_rank_fwd_bf16(const AttnArgs& a, const RankKV& rk, int dqk, int dv, bool out_bf16,
+                                hipStream_t st) {
+  if (dqk == 128 && dv == 128) return launch_t<128, 128>(a, &rk, true, false, out_bf16, st);
+  if (dqk == 192 && dv == 128) return launch_t<192, 128>(a, &rk, true, false, out_bf16, st);
+  if (dqk == 64 && dv == 64) return launch_t<64, 64>(a, &rk, true, false, out_bf16, st);
   return hipErrorInvalidValue;
 }
 

@@ -47,6 +47,14 @@ struct AttnArgs {
   float* dv;              // [total_k, hkv, dv] fp32 accumulate
 };
 
+// KV blocks of every owner for a rank's fused forward (one launch per rank).
+constexpr int kMaxCp = 64;
+struct RankKV {
+  const void* k[kMaxCp];
+  const void* v[kMaxCp];
+  int32_t cp, rank;
+};
+
 // Segment part [lo, hi) after applying a zig-zag half selector.
 __host__ __device__ inline void part_range(int32_t s0, int32_t s1, int32_t part, int32_t* lo,
                                            int32_t* hi) {
@@ -66,6 +74,8 @@ __host__ __device__ inline void part_range(int32_t s0, int32_t s1, int32_t part,
 // Launchers (return hipError_t of the launch).
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int dqk, int dv, bool causal, bool merge,
                                 hipStream_t st);
+hipError_t launch_rank_fwd_bf16(const AttnArgs& a, const RankKV& rk, int dqk, int dv,
+                                bool out_bf16, hipStream_t st);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, int dqk, int dv, bool causal, bool merge,
                                hipStream_t st);
 hipError_t launch_lse_merge(float* out_acc, float* lse_acc, const float* out_part,

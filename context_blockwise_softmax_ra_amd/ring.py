@@ -81,12 +81,12 @@ class RingProblem:
                            k_part=k_part, causal=causal, scale=self.scale)
 
     def forward_desc(self, r: int, out: torch.Tensor, lse: torch.Tensor,
-                     workspace: Optional[torch.Tensor] = None, fuse_merge: bool = False,
+                     workspace: Optional[torch.Tensor] = None, fuse_merge: int = 0,
                      events=None) -> L.RankDesc:
         return L.rank_desc(self.local_desc(r), self.cp, r, self.k, self.v, out, lse, workspace,
                            fuse_merge, events)
 
-    def alloc_forward(self, out_dtype=torch.bfloat16, fuse_merge=False):
+    def alloc_forward(self, out_dtype=torch.bfloat16, fuse_merge=0):
         dev = self.q[0].device
         out = torch.empty((self.Tl, self.hq, self.dv), dtype=out_dtype, device=dev)
         lse = torch.empty((self.hq, self.Tl), dtype=torch.float32, device=dev)
@@ -94,7 +94,7 @@ class RingProblem:
         ws = torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
         return out, lse, ws
 
-    def forward(self, r: int, out, lse, ws, fuse_merge=False, events=None, stream=None):
+    def forward(self, r: int, out, lse, ws, fuse_merge=0, events=None, stream=None):
         L.ra_rank_forward(self.forward_desc(r, out, lse, ws, fuse_merge, events), stream)
 
     def backward_desc(self, r, out, lse, dq, dk_blocks, dv_blocks, workspace, events=None):

@@ -81,7 +81,7 @@ typedef enum {
  * softmax_scale <= 0 selects 1/sqrt(dqk).
  *
  * Supported: bf16 with (dqk, dv) in {(64,64), (128,128), (192,128)};
- * fp32 with dqk, dv <= 128 and multiples of 4.
+ * fp32 with dqk == dv in {16, 32, 64, 128}.
  */
 typedef struct ra_attn_desc {
   const void* q;
@@ -181,9 +181,14 @@ ra_status ra_cast_f32_bf16(const float* src, void* dst, int64_t n, void* stream)
  * k_blocks / v_blocks: host arrays [cp_size] of device pointers, by owner.
  * out [total_q, hq, dv] of out_dtype, lse [hq, total_q] float32: final.
  * fuse_merge = 0: each step writes a partial to the workspace and
- * ra_lse_merge folds it; 1: steps merge in the attention epilogue.
+ * ra_lse_merge folds it; 1: steps merge in the attention epilogue;
+ * 2 (bf16): the whole share in one launch, every owner's block walked in
+ * ring order with the online-softmax state kept in registers and the final
+ * output written by the epilogue (the pass-KV form of the oh-bug page with
+ * all blocks resident; no workspace).  fp32 falls back to 1.
  * events (optional): host array of 2*cp_size hipEvent_t, recorded on the
- * stream right before / after step s's attention launch.
+ * stream right before / after step s's attention launch (with
+ * fuse_merge = 2 only events[0], events[1], around the single launch).
  */
 typedef struct ra_rank_desc {
   ra_attn_desc local;

@@ -226,7 +226,7 @@ def test_tiny_fp32_workload_steps_ranks_and_concat():
     q64, k64, v64 = to_np(q), to_np(k), to_np(v)
     cu = w.cu_global()
     full_o, full_l = oracle.full_attention(q64, k64, v64, cu)
-    for fuse in (False, True):
+    for fuse in (0, 1, 2):
         outs, lses = _run_all_ranks(prob, torch.float32, fuse)
         cat_o = np.zeros_like(full_o)
         cat_l = np.zeros_like(full_l)
@@ -257,7 +257,7 @@ def test_tiny_fp32_workload_steps_ranks_and_concat():
             check_lse(gl[:, cov], rl[:, cov], f"rank{r} step{s}", tol=1e-5)
 
 
-def _full_parity(w, fuse_modes=(False, True), determinism=False):
+def _full_parity(w, fuse_modes=(0, 1, 2), determinism=False):
     log(f"workload {w.name}: S={w.seqlen} C={w.cp} hq={w.hq} hkv={w.hkv} d={w.dqk}/{w.dv}")
     prob, (q, k, v, _) = make_problem(w)
     q64, k64, v64 = to_np(q), to_np(k), to_np(v)
@@ -315,10 +315,16 @@ def _sampled_parity(w, ranks, n_rows=40, fuse=False):
 
 def test_gqa_32k_workload_sampled():
     _sampled_parity(synth.WORKLOADS["gqa_32k"], ranks=(0, 3, 7))
+    _sampled_parity(synth.WORKLOADS["gqa_32k"], ranks=(5,), fuse=2)
 
 
 def test_varlen_128k_workload_sampled():
-    _sampled_parity(synth.WORKLOADS["varlen_128k"], ranks=(0, 7, 15), fuse=True)
+    _sampled_parity(synth.WORKLOADS["varlen_128k"], ranks=(0, 7, 15), fuse=1)
+    _sampled_parity(synth.WORKLOADS["varlen_128k"], ranks=(3, 12), fuse=2)
+
+
+def test_mla_256k_forward_sampled():
+    _sampled_parity(synth.WORKLOADS["mla_256k"], ranks=(0, 31), n_rows=16, fuse=2)
 
 
 def test_rank_accounting_matches_oracle_pairs():
