@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--fuse-merge", type=int, default=2,
                     help="0: per-step partials + ra_lse_merge; 1: merge in the attention "
                          "epilogue; 2: the whole rank share in one launch")
+    ap.add_argument("--kernel", default="auto", choices=("auto", "4w", "pp"),
+                    help="bf16 forward kernel: chosen by launch size (auto), the 4-wave "
+                         "kernel, or the 8-wave ping-pong kernel")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the oracle CPU baseline sample (0 = skip)")
     ap.add_argument("--backward", type=int, default=0,
@@ -67,21 +70,25 @@ def copy_calibration(mib: int):
                       "launches": 3}), flush=True)
 
 
-def kernel_hash() -> str:
-    p = os.path.join(ROOT, "context_blockwise_softmax_ra_amd", "csrc", "attn_fwd_bf16.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+def kernel_hash(kernel: str) -> str:
+    """Hash of the sources a forward kernel is built from."""
+    csrc = os.path.join(ROOT, "context_blockwise_softmax_ra_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("mfma_common.h", "fwd_tiles.h", kernel + ".hip"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
-def traffic_for(workload: str):
+def traffic_for(workload: str, kernel: str):
     """HBM bytes per attention launch from committed counter runs, if still current."""
-    p = os.path.join(ROOT, "profiles", f"traffic_attn_fwd_bf16_{workload}.json")
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(p):
         return None
     try:
         t = json.load(open(p))
     except Exception:
         return None
-    if t.get("kernel_sha256_16") != kernel_hash():
+    if t.get("kernel_sha256_16") != kernel_hash(kernel):
         return None
     return t.get("bytes_per_launch")
 
@@ -202,6 +209,10 @@ def main():
     if a.copy_calibration_mib:
         copy_calibration(a.copy_calibration_mib)
         return
+    if a.kernel != "auto":
+        os.environ["RA_FWD_KERNEL"] = a.kernel
+    else:
+        os.environ.pop("RA_FWD_KERNEL", None)
     import numpy as np
     import torch
     import synth
@@ -291,7 +302,13 @@ def main():
     achieved = attn_flops / (attn_ms / 1e3) / 1e12
     avg_launch_ms = attn_ms / n_launch
     value = step_flops / (ms_step / 1e3) / 1e12
-    traffic = traffic_for(w.name)
+    if a.fuse_merge == 2:
+        kname = L.ra_forward_kernel(prob.local_desc(0), L.PART_ALL)
+    else:
+        names = {L.ra_forward_kernel(prob.step_desc(0, j, c, qp, kp), qp)
+                 for (j, c, qp, kp) in prob.step_plan(0)}
+        kname = "/".join(sorted(names))
+    traffic = traffic_for(w.name, kname) if a.fuse_merge == 2 else None
 
     res = {
         "metric": "effective attention TFLOP/s per rank-share (bf16) + % of MFMA peak, 1 GPU",
@@ -317,7 +334,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_fwd_bf16" + (" (whole rank share per launch)" if a.fuse_merge == 2 else ""),
+            "kernel": kname + (" (whole rank share per launch)" if a.fuse_merge == 2 else ""),
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

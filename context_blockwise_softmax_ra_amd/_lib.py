@@ -28,7 +28,7 @@ EXPORTS = (
     "ra_block_attn_fwd", "ra_block_attn_fwd_merge", "ra_lse_merge", "ra_zigzag_shard_map",
     "ra_zigzag_gather", "ra_zigzag_scatter", "ra_cast_f32_bf16", "ra_rank_forward_workspace",
     "ra_rank_forward", "ra_attn_bwd_delta", "ra_block_attn_bwd", "ra_rank_backward_workspace",
-    "ra_rank_backward", "ra_block_attn_work", "ra_last_error", "ra_version",
+    "ra_rank_backward", "ra_block_attn_work", "ra_forward_kernel", "ra_last_error", "ra_version",
 )
 
 
@@ -116,6 +116,8 @@ def lib():
             f = getattr(L, name)
             f.argtypes = args
             f.restype = c_int
+        L.ra_forward_kernel.argtypes = [POINTER(AttnDesc), c_int]
+        L.ra_forward_kernel.restype = c_char_p
         L.ra_last_error.argtypes = []
         L.ra_last_error.restype = c_char_p
         L.ra_version.argtypes = []
@@ -354,6 +356,14 @@ def ra_block_attn_work(desc: AttnDesc):
     _check(lib().ra_block_attn_work(ctypes.byref(desc), ctypes.byref(a), ctypes.byref(b),
                                     ctypes.byref(c)))
     return a.value, b.value, c.value
+
+
+def ra_forward_kernel(desc: AttnDesc, q_part: int = PART_ALL) -> str:
+    """Name of the forward kernel a launch over q_part of ``desc`` uses."""
+    r = lib().ra_forward_kernel(ctypes.byref(desc), q_part)
+    if r is None:
+        raise RaError(1, lib().ra_last_error().decode())
+    return r.decode()
 
 
 def ra_last_error() -> str:

@@ -43,6 +43,7 @@ def sources():
 # results in VGPRs.
 PER_FILE = {
     "attn_fwd_bf16.hip": ["-fno-honor-nans"],
+    "attn_fwd_pp.hip": ["-fno-honor-nans"],
     "attn_bwd_bf16.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 

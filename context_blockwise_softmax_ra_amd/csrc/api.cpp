@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -152,15 +153,40 @@ ra::AttnArgs make_args(const ra_attn_desc* d, const Checked& c) {
   return a;
 }
 
+// Which bf16 forward kernel runs a launch.  The 8-wave ping-pong kernel
+// works on 256-row query tiles and pays off when its matrix-core phase and
+// softmax phase are of similar length and the tiles are full: head dims
+// 128/128, at least two 256-row tiles (x query heads) per CU of the 256,
+// and at most 1/8 of the tiled rows being padding (short packed documents
+// leave most of a 256-row tile idle).  Otherwise the 4-wave kernel (128-row
+// tiles) runs.  RA_FWD_KERNEL=pp or =4w in the environment forces one.
+bool use_pingpong(const ra_attn_desc* d, ra_part q_part) {
+  const char* e = std::getenv("RA_FWD_KERNEL");
+  if (e && !std::strcmp(e, "pp")) return true;
+  if (e && !std::strcmp(e, "4w")) return false;
+  if (d->dqk != 128 || d->dv != 128) return false;
+  long long tiles = 0, rows = 0;
+  for (int s = 0; s < d->n_seq; ++s) {
+    const int lq = part_len(d->cu_seqlens_q_host[s + 1] - d->cu_seqlens_q_host[s], q_part);
+    tiles += (lq + 255) / 256;
+    rows += lq;
+  }
+  return tiles * d->hq >= 2 * 256 && tiles * 256 * 7 <= rows * 8;
+}
+
 ra_status launch_fwd(const ra_attn_desc* d, const Checked& c, float* out, float* lse, bool merge,
                      hipStream_t st) {
   ra::AttnArgs a = make_args(d, c);
   a.out = out;
   a.lse = lse;
   if (a.n_qtiles == 0) return RA_OK;
-  hipError_t e = d->dtype == RA_BF16
-                     ? ra::launch_attn_fwd_bf16(a, d->dqk, d->dv, d->causal != 0, merge, st)
-                     : ra::launch_attn_fwd_f32(a, d->dqk, d->dv, d->causal != 0, merge, st);
+  hipError_t e;
+  if (d->dtype != RA_BF16)
+    e = ra::launch_attn_fwd_f32(a, d->dqk, d->dv, d->causal != 0, merge, st);
+  else if (use_pingpong(d, d->q_part))
+    e = ra::launch_attn_fwd_pp(a, d->dqk, d->dv, d->causal != 0, merge, st);
+  else
+    e = ra::launch_attn_fwd_bf16(a, d->dqk, d->dv, d->causal != 0, merge, st);
   if (e != hipSuccess) return hip_fail(e, "attention forward launch");
   return RA_OK;
 }
@@ -252,6 +278,28 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 }  // namespace
 
 extern "C" {
+
+const char* ra_forward_kernel(const ra_attn_desc* d, ra_part q_part) {
+  if (!d) {
+    fail(RA_ERR_INVALID_ARG, "descriptor is NULL");
+    return nullptr;
+  }
+  if (q_part < RA_PART_ALL || q_part > RA_PART_SECOND_HALF) {
+    fail(RA_ERR_INVALID_ARG, "unknown part selector");
+    return nullptr;
+  }
+  if (d->dtype != RA_BF16 && d->dtype != RA_FP32) {
+    fail(RA_ERR_INVALID_ARG, "unknown dtype");
+    return nullptr;
+  }
+  if (d->n_seq <= 0 || !d->cu_seqlens_q_host) {
+    fail(RA_ERR_INVALID_ARG, "n_seq or cu_seqlens_q_host invalid");
+    return nullptr;
+  }
+  if (check_cu(d->cu_seqlens_q_host, d->n_seq, "cu_seqlens_q_host") != RA_OK) return nullptr;
+  if (d->dtype == RA_FP32) return "attn_fwd_f32";
+  return use_pingpong(d, q_part) ? "attn_fwd_pp" : "attn_fwd_bf16";
+}
 
 const char* ra_last_error(void) { return g_err.c_str(); }
 
@@ -439,7 +487,9 @@ ra_status ra_rank_forward(const ra_rank_desc* d, void* stream) {
         (e = hipEventRecord((hipEvent_t)d->events[0], hs)) != hipSuccess)
       return hip_fail(e, "event record");
     if (a.n_qtiles > 0) {
-      e = ra::launch_rank_fwd_bf16(a, rk, L.dqk, L.dv, d->out_dtype == RA_BF16, hs);
+      e = use_pingpong(&L, RA_PART_ALL)
+              ? ra::launch_rank_fwd_pp(a, rk, L.dqk, L.dv, d->out_dtype == RA_BF16, hs)
+              : ra::launch_rank_fwd_bf16(a, rk, L.dqk, L.dv, d->out_dtype == RA_BF16, hs);
       if (e != hipSuccess) return hip_fail(e, "rank forward launch");
     }
     if (d->events && d->events[1] &&

@@ -30,31 +30,24 @@
 // 8 consecutive keys.  V stays row-major in LDS and the V^T operand is read
 // with the gfx950 transposing LDS read (ds_read_b64_tr_b16).
 //
-// K/V tiles go from global memory straight into LDS (global_load_lds_dwordx4:
-// each wave instruction fills 1 KiB of LDS, lane i writing bytes 16i..16i+15),
-// double-buffered: tile t+1 streams in while tile t is computed, with one
-// barrier per tile.  Because the LDS destination of a lane is fixed, bank
-// spreading is done by choosing which global 16-byte chunk each lane
-// fetches (an XOR swizzle), with 64 banks x 4 bytes in mind:
-//   K: 64-dim panels of 128-byte rows, chunk slot = chunk ^ ((row>>1)&7);
-//      the 16 rows a 128-bit read serves at once land on 16 distinct slots.
-//   V: 256-byte rows, chunk slot = chunk ^ (((row&3)<<2)|((row>>2)&3)); the
-//      4 rows x 64 bytes of one transposing read land on 16 distinct slots.
+// K/V tiles go from global memory straight into LDS with the XOR-swizzled
+// layouts of fwd_tiles.h, double-buffered: tile t+1 streams in while tile t
+// is computed, with one barrier per tile.
 //
 // Blocks are remapped so that each of the 8 XCDs gets a contiguous range of
 // tiles ordered (segment, kv head, query tile, head in group): the query
 // heads sharing a kv head, and neighbouring query tiles, read the same K/V
 // through the same L2.  Causal launches order query tiles heaviest first.
 
-#include "mfma_common.h"
+#include "fwd_tiles.h"
 
 namespace ra {
 namespace {
 
 using namespace mfma;
+using namespace fwd;
 
 constexpr int BM = kFwdBlockM;
-constexpr int BN = kFwdBlockN;
 constexpr int NW = kFwdWaves;
 constexpr int NT = NW * 64;
 
@@ -64,117 +57,17 @@ constexpr int NT = NW * 64;
 // use the same (possibly stale) max; p stays <= 2^8.
 constexpr float kRescaleLog2 = 8.0f;
 
-template <int DQK, int DV>
-struct Geo {
-  static constexpr int KPANELS = DQK / 64;               // 64-dim panels of K
-  static constexpr int KPANEL_BYTES = BN * 128;
-  static constexpr int K_BYTES = KPANELS * KPANEL_BYTES;
-  static constexpr int VROWB = DV * 2;                   // 256 (DV=128) or 128 (DV=64)
-  static constexpr int V_BYTES = BN * VROWB;
-  static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int K_INST = K_BYTES / 1024;          // wave instructions per K tile
-  static constexpr int V_INST = V_BYTES / 1024;
-  static constexpr int KK = DQK / 16;                    // MFMA k-steps for S
-  static constexpr int OT = DV / 32;                     // output tiles per wave
-  static_assert(K_INST % NW == 0 && V_INST % NW == 0, "tile load split");
-  static_assert(DV == 128 || DV == 64, "V layouts");
-};
-
-__device__ __forceinline__ int k_slot(int row, int c) { return c ^ ((row >> 1) & 7); }
-
-// V chunk slot: 256-byte rows use the dual swizzle; 128-byte rows flip the
-// 64-byte half on alternate row pairs.
-template <int VROWB>
-__device__ __forceinline__ int v_slot(int row, int c) {
-  return VROWB == 256 ? (c ^ swz(row)) : (c ^ (((row >> 1) & 1) << 2));
-}
-
-template <int VROWB>
-__device__ __forceinline__ int v_off(int row, int byte) {
-  return row * VROWB + (v_slot<VROWB>(row, byte >> 4) << 4) + (byte & 15);
-}
-
-__device__ __forceinline__ void g2lds(const void* g, char* lds) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-}
-
-// This wave's share of the direct global->LDS loads of one K/V tile: per
-// instruction a per-lane byte offset (fixed for the whole launch) from the
-// tile's base row, and a wave-uniform LDS destination.
-template <int DQK, int DV>
-struct TileLoader {
-  using G = Geo<DQK, DV>;
-  static constexpr int KI = G::K_INST / NW, VI = G::V_INST / NW;
-  static constexpr int VCH = G::VROWB / 16, RPI = 1024 / G::VROWB;
-  uint32_t koff[KI], voff[VI];  // byte offsets from the tile's first key row
-  int wave, lane;
-
-  __device__ __forceinline__ int krow(int jj) const { return ((wave + NW * jj) % (BN / 8)) * 8 + (lane >> 3); }
-  __device__ __forceinline__ int kcol(int jj) const {
-    return ((wave + NW * jj) / (BN / 8) * 64 + k_slot(krow(jj), lane & 7) * 8) * 2;  // XOR involution
-  }
-  __device__ __forceinline__ int kdst(int jj) const {
-    const int j = wave + NW * jj;
-    return j / (BN / 8) * G::KPANEL_BYTES + (j % (BN / 8)) * 1024;
-  }
-  __device__ __forceinline__ int vrow(int jj) const { return (wave + NW * jj) * RPI + lane / VCH; }
-  __device__ __forceinline__ int vcol(int jj) const { return v_slot<G::VROWB>(vrow(jj), lane % VCH) * 16; }
-  __device__ __forceinline__ int vdst(int jj) const { return G::K_BYTES + (wave + NW * jj) * 1024; }
-
-  __device__ __forceinline__ void init(int64_t ks_bytes, int64_t vs_bytes, int w, int l) {
-    wave = w;
-    lane = l;
-#pragma unroll
-    for (int jj = 0; jj < KI; ++jj) koff[jj] = (uint32_t)(krow(jj) * ks_bytes + kcol(jj));
-#pragma unroll
-    for (int jj = 0; jj < VI; ++jj) voff[jj] = (uint32_t)(vrow(jj) * vs_bytes + vcol(jj));
-  }
-
-  // rows_left: key rows available from the tile's first row on (clamp the last tile only)
-  __device__ __forceinline__ void issue(const char* kt, const char* vt, int64_t ks_bytes,
-                                        int64_t vs_bytes, int rows_left, char* stage) const {
-    if (rows_left >= BN) {
-#pragma unroll
-      for (int jj = 0; jj < KI; ++jj) g2lds(kt + koff[jj], stage + kdst(jj));
-#pragma unroll
-      for (int jj = 0; jj < VI; ++jj) g2lds(vt + voff[jj], stage + vdst(jj));
-    } else {
-#pragma unroll
-      for (int jj = 0; jj < KI; ++jj)
-        g2lds(kt + min(krow(jj), rows_left - 1) * ks_bytes + kcol(jj), stage + kdst(jj));
-#pragma unroll
-      for (int jj = 0; jj < VI; ++jj)
-        g2lds(vt + min(vrow(jj), rows_left - 1) * vs_bytes + vcol(jj), stage + vdst(jj));
-    }
-  }
-};
-
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  return __builtin_fmaxf(a, __builtin_fmaxf(b, c));
-}
-
-// How a KV block meets the rows of a workgroup.
-enum BlockKind {
-  KIND_CAUSAL = 0,     // key j visible to row i iff j <= i (part-relative)
-  KIND_ALL = 1,        // every key visible
-  KIND_LATE_ROWS = 2,  // every key visible to rows of the segment's second half only
-};
-
-struct Block {
-  const char* kb;  // K of the block's first key (this kv head)
-  const char* vb;
-  int klen;
-  int kind;
-  int ntiles;
-};
-
 // MODE: 0 = one non-causal block, 1 = one causal block (both as described by
 // the AttnArgs parts), 2 = a rank's whole share: the C blocks of RankKV in
 // ring order, merged in registers (no partials, no separate merge).
 template <int DQK, int DV, int MODE, bool MERGE, bool OUT_BF16>
 __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV rk) {
   using G = Geo<DQK, DV>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * G::STAGE];
+  // two stages as separate objects: the compiler can then tell that the
+  // direct loads into one stage never alias the reads of the other, and
+  // does not wait for the prefetch before reading the current tile
+  __shared__ __attribute__((aligned(1024))) char smem0[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem1[G::STAGE];
 
   const int nb = gridDim.x;
   int b = xcd_remap(blockIdx.x, nb);
@@ -211,6 +104,9 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
   const int my_row_rel = my_row - q_lo;
   const int64_t ks_bytes = a.k_stride * 2, vs_bytes = a.v_stride * 2;
   const int nblocks = MODE == 2 ? rk.cp : 1;
+  // key segment bounds, read once: a vector load inside the tile loop would
+  // make the wave wait for its outstanding prefetch
+  const int kseg0 = a.cu_k[seg], kseg1 = a.cu_k[seg + 1];
 
   // block bi of this workgroup, with the number of key tiles it visits
   auto get_block = [&](int bi) -> Block {
@@ -233,7 +129,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
       kpart = a.k_part;
     }
     int k_lo, k_hi;
-    part_range(a.cu_k[seg], a.cu_k[seg + 1], kpart, &k_lo, &k_hi);
+    part_range(kseg0, kseg1, kpart, &k_lo, &k_hi);
     blk.klen = k_hi - k_lo;
     blk.kb = reinterpret_cast<const char*>(kp) + ((int64_t)k_lo * a.k_stride + (int64_t)kvh * DQK) * 2;
     blk.vb = reinterpret_cast<const char*>(vp) + ((int64_t)k_lo * a.v_stride + (int64_t)kvh * DV) * 2;
@@ -268,18 +164,19 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
   for (int bi = 0; bi < nblocks; ++bi) total += get_block(bi).ntiles;
   if (total == 0 && MERGE) return;  // merging an empty block is the identity
 
-  TileLoader<DQK, DV> ld;
+  TileLoader<DQK, DV, NW> ld;
   ld.init(ks_bytes, vs_bytes, wave, lane);
   Cursor lc, cc;
   first(lc);
   cc = lc;
   auto issue_next = [&](char* stage) {
-    ld.issue(lc.blk.kb + (int64_t)lc.t * BN * ks_bytes, lc.blk.vb + (int64_t)lc.t * BN * vs_bytes,
-             ks_bytes, vs_bytes, lc.blk.klen - lc.t * BN, stage);
+    ld.issue_k(lc.blk.kb + (int64_t)lc.t * BN * ks_bytes, ks_bytes, lc.blk.klen - lc.t * BN, stage);
+    ld.issue_v(lc.blk.vb + (int64_t)lc.t * BN * vs_bytes, vs_bytes, lc.blk.klen - lc.t * BN,
+               stage + G::K_BYTES);
     advance(lc);
   };
   // the first K/V tile streams in while Q is fetched
-  if (total > 0) issue_next(smem);
+  if (total > 0) issue_next(smem0);
 
   // Q^T operand: lane holds row my_row, dims 16*kk + 8*g .. +7
   bf16x8 qf[G::KK];
@@ -409,8 +306,8 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
     __syncthreads();
   };
   for (int gi = 0; gi < total; gi += 2) {
-    tile(gi, smem, smem + G::STAGE);
-    if (gi + 1 < total) tile(gi + 1, smem + G::STAGE, smem);
+    tile(gi, smem0, smem1);
+    if (gi + 1 < total) tile(gi + 1, smem1, smem0);
   }
 
   if (!wave_live || my_row >= q_hi) return;

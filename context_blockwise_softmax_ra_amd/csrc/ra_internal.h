@@ -76,6 +76,10 @@ hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int dqk, int dv, bool causal,
                                 hipStream_t st);
 hipError_t launch_rank_fwd_bf16(const AttnArgs& a, const RankKV& rk, int dqk, int dv,
                                 bool out_bf16, hipStream_t st);
+hipError_t launch_attn_fwd_pp(const AttnArgs& a, int dqk, int dv, bool causal, bool merge,
+                              hipStream_t st);
+hipError_t launch_rank_fwd_pp(const AttnArgs& a, const RankKV& rk, int dqk, int dv,
+                              bool out_bf16, hipStream_t st);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, int dqk, int dv, bool causal, bool merge,
                                hipStream_t st);
 hipError_t launch_lse_merge(float* out_acc, float* lse_acc, const float* out_part,

@@ -264,6 +264,20 @@ ra_status ra_rank_backward(const ra_rank_bwd_desc* d, void* stream);
 ra_status ra_block_attn_work(const ra_attn_desc* d, int64_t* visible_pairs,
                              int64_t* tiles_visited, int64_t* tiles_skipped);
 
+/*
+ * Name of the bf16 forward kernel a launch over the rows of q_part of `d`
+ * uses (ra_block_attn_fwd / _merge with d->q_part, ra_rank_forward with
+ * fuse_merge = 2 and RA_PART_ALL): "attn_fwd_pp" (8 waves, 256-row query
+ * tiles, matrix-core and softmax phases of the two waves of a SIMD
+ * interleaved) for head dims 128/128 when the launch has at least 512 such
+ * tiles over all query heads and at most 1/8 of the tiled rows are padding,
+ * "attn_fwd_bf16" (4 waves, 128-row tiles) otherwise, "attn_fwd_f32" for
+ * float32.  Both bf16 kernels compute the same result.  The environment
+ * variable RA_FWD_KERNEL=pp or =4w forces one.  Host only; NULL (with
+ * ra_last_error set) for an invalid descriptor.
+ */
+const char* ra_forward_kernel(const ra_attn_desc* d, ra_part q_part);
+
 /* Thread-local description of the last non-OK status ("" if none). */
 const char* ra_last_error(void);
 

@@ -241,3 +241,32 @@ def test_binding_rejects_non_contiguous_buffers():
     assert L._ptr(ok, True) == ok.data_ptr()
     with pytest.raises(ValueError):
         L._ptr(np.zeros((3, 4)).T)
+
+
+# ---------------------------------------------------------------------------
+# forward kernel choice (host only)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,expect", [("tiny_fp32", "attn_fwd_f32"), ("mha_8k", "attn_fwd_bf16"),
+                                         ("gqa_32k", "attn_fwd_pp"), ("varlen_128k", "attn_fwd_bf16"),
+                                         ("mla_256k", "attn_fwd_bf16")])
+def test_forward_kernel_choice_per_workload(name, expect, monkeypatch):
+    monkeypatch.delenv("RA_FWD_KERNEL", raising=False)
+    w = synth.WORKLOADS[name]
+    cu_local, _ = L.ra_zigzag_shard_map(w.cp, 0, w.cu_global())
+    d = _desc(hq=w.hq, hkv=w.hkv, dqk=w.dqk, dv=w.dv, cu=cu_local,
+              dtype=L.RA_FP32 if w.dtype == "fp32" else L.RA_BF16)
+    assert L.ra_forward_kernel(d, L.PART_ALL) == expect
+    if expect != "attn_fwd_f32":
+        monkeypatch.setenv("RA_FWD_KERNEL", "pp")
+        assert L.ra_forward_kernel(d, L.PART_ALL) == "attn_fwd_pp"
+        monkeypatch.setenv("RA_FWD_KERNEL", "4w")
+        assert L.ra_forward_kernel(d, L.PART_ALL) == "attn_fwd_bf16"
+
+
+def test_forward_kernel_choice_rejects_bad_input():
+    d = _desc()
+    with pytest.raises(L.RaError):
+        L.ra_forward_kernel(d, 7)
+    assert L.lib().ra_forward_kernel(None, 0) is None
+    assert "NULL" in L.ra_last_error()

@@ -6,6 +6,8 @@ finalisation, and whole rank shares for the five workloads (in full where
 the oracle finishes in seconds, else reduced sizes in full plus sampled
 rows at full size).
 """
+import contextlib
+import os
 import zlib
 
 import numpy as np
@@ -23,6 +25,27 @@ R = pytest.importorskip("context_blockwise_softmax_ra_amd")
 from context_blockwise_softmax_ra_amd import _lib as L  # noqa: E402
 
 DEV = torch.device("cuda:0")
+
+# The library picks the bf16 forward kernel by launch size (the 4-wave kernel
+# with 128-row tiles, or the 8-wave ping-pong kernel with 256-row tiles);
+# RA_FWD_KERNEL forces one, so every case runs on both.
+KERNELS = ("4w", "pp")
+
+
+@contextlib.contextmanager
+def fwd_kernel(name):
+    old = os.environ.get("RA_FWD_KERNEL")
+    if name is None:
+        os.environ.pop("RA_FWD_KERNEL", None)
+    else:
+        os.environ["RA_FWD_KERNEL"] = name
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop("RA_FWD_KERNEL", None)
+        else:
+            os.environ["RA_FWD_KERNEL"] = old
 
 
 # ---------------------------------------------------------------------------
@@ -90,12 +113,14 @@ def _cu(lengths):
     return synth.cu_seqlens(lengths)
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("dims", [(128, 128), (192, 128), (64, 64)])
 @pytest.mark.parametrize("case", EDGE_CASES, ids=[c[0] for c in EDGE_CASES])
-def test_block_fwd_bf16_edge_cases(case, dims):
+def test_block_fwd_bf16_edge_cases(case, dims, kernel, monkeypatch):
     name, lq, lk, qp, kp, causal, hq, hkv = case
     dqk, dv = dims
-    log(f"case {name} dims {dims}")
+    monkeypatch.setenv("RA_FWD_KERNEL", kernel)
+    log(f"case {name} dims {dims} kernel {kernel}")
     cu_q, cu_k = _cu(lq), _cu(lk)
     g = torch.Generator().manual_seed(zlib.crc32(f"{name}{dims}".encode()) & 0xFFFF)
     q = torch.randn(int(cu_q[-1]), hq, dqk, generator=g).to(torch.bfloat16)
@@ -262,16 +287,20 @@ def _full_parity(w, fuse_modes=(0, 1, 2), determinism=False):
     prob, (q, k, v, _) = make_problem(w)
     q64, k64, v64 = to_np(q), to_np(k), to_np(v)
     ro, rl = oracle.full_attention(q64, k64, v64, w.cu_global())
-    for fuse in fuse_modes:
-        outs, lses = _run_all_ranks(prob, torch.bfloat16, fuse)
-        for r in range(w.cp):
-            rows = prob.rows(r)
-            check_out(outs[r], ro[rows], w.dtype, f"rank{r} fuse={fuse}")
-            check_lse(lses[r], rl[:, rows], f"rank{r} fuse={fuse}")
-        if determinism:
-            again, again_l = _run_all_ranks(prob, torch.bfloat16, fuse)
+    for kernel in KERNELS:
+        for fuse in fuse_modes:
+            tag = f"fuse={fuse} kernel={kernel}"
+            with fwd_kernel(kernel):
+                outs, lses = _run_all_ranks(prob, torch.bfloat16, fuse)
             for r in range(w.cp):
-                assert np.array_equal(outs[r], again[r]) and np.array_equal(lses[r], again_l[r])
+                rows = prob.rows(r)
+                check_out(outs[r], ro[rows], w.dtype, f"rank{r} {tag}")
+                check_lse(lses[r], rl[:, rows], f"rank{r} {tag}")
+            if determinism:
+                with fwd_kernel(kernel):
+                    again, again_l = _run_all_ranks(prob, torch.bfloat16, fuse)
+                for r in range(w.cp):
+                    assert np.array_equal(outs[r], again[r]) and np.array_equal(lses[r], again_l[r])
     return prob
 
 
@@ -293,8 +322,8 @@ def test_mla_forward_reduced_full_parity():
     _full_parity(synth.reduced("mla_256k", 4096, 8))
 
 
-def _sampled_parity(w, ranks, n_rows=40, fuse=False):
-    log(f"workload {w.name} (full size, sampled rows): S={w.seqlen} C={w.cp}")
+def _sampled_parity(w, ranks, n_rows=40, fuse=False, kernel=None):
+    log(f"workload {w.name} (full size, sampled rows): S={w.seqlen} C={w.cp} kernel={kernel}")
     prob, (q, k, v, _) = make_problem(w)
     q64 = to_np(q)
     k64, v64 = to_np(k), to_np(v)
@@ -302,7 +331,8 @@ def _sampled_parity(w, ranks, n_rows=40, fuse=False):
     cu = w.cu_global()
     for r in ranks:
         out, lse, ws = prob.alloc_forward(torch.bfloat16, fuse)
-        prob.forward(r, out, lse, ws, fuse_merge=fuse)
+        with fwd_kernel(kernel):
+            prob.forward(r, out, lse, ws, fuse_merge=fuse)
         torch.cuda.synchronize()
         loc = sample_rows(prob, r, n_rows)
         glob = prob.rows(r)[loc]
@@ -316,15 +346,18 @@ def _sampled_parity(w, ranks, n_rows=40, fuse=False):
 def test_gqa_32k_workload_sampled():
     _sampled_parity(synth.WORKLOADS["gqa_32k"], ranks=(0, 3, 7))
     _sampled_parity(synth.WORKLOADS["gqa_32k"], ranks=(5,), fuse=2)
+    _sampled_parity(synth.WORKLOADS["gqa_32k"], ranks=(2,), fuse=2, kernel="4w")
 
 
 def test_varlen_128k_workload_sampled():
     _sampled_parity(synth.WORKLOADS["varlen_128k"], ranks=(0, 7, 15), fuse=1)
     _sampled_parity(synth.WORKLOADS["varlen_128k"], ranks=(3, 12), fuse=2)
+    _sampled_parity(synth.WORKLOADS["varlen_128k"], ranks=(9,), fuse=2, kernel="pp")
 
 
 def test_mla_256k_forward_sampled():
     _sampled_parity(synth.WORKLOADS["mla_256k"], ranks=(0, 31), n_rows=16, fuse=2)
+    _sampled_parity(synth.WORKLOADS["mla_256k"], ranks=(17,), n_rows=16, fuse=2, kernel="4w")
 
 
 def test_rank_accounting_matches_oracle_pairs():
