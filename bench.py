@@ -44,6 +44,10 @@ def parse():
     ap.add_argument("--fuse-merge", type=int, default=2,
                     help="0: per-step partials + ra_lse_merge; 1: merge in the attention "
                          "epilogue; 2: the whole rank share in one launch")
+    ap.add_argument("--mode", default="ring", choices=("ring", "ulysses"),
+                    help="ring: zig-zag ring-attention rank shares (the headline); ulysses: "
+                         "the Ulysses rank shares of the same workload (all tokens, Hq/C "
+                         "heads each) on the same kernels, with the per-rank work of both")
     ap.add_argument("--kernel", default="auto", choices=("auto", "4w", "pp"),
                     help="bf16 forward kernel: chosen by launch size (auto), the 4-wave "
                          "kernel, or the 8-wave ping-pong kernel")
@@ -200,6 +204,65 @@ def bench_backward(a, w, prob, torch, L):
     print(json.dumps(res), flush=True)
 
 
+def bench_ulysses(a, w, q, k, v, torch, L):
+    """Forward step: every rank's Ulysses share (one causal launch over a head slice)."""
+    from context_blockwise_softmax_ra_amd.ulysses import UlyssesProblem
+    C = w.cp
+    uly = UlyssesProblem(q, k, v, w.cu_global(), C)
+    bufs = [uly.alloc_forward() for _ in range(C)]
+    fl_pair = 2 * (w.dqk + w.dv)
+    work = [uly.work(r) for r in range(C)]
+    step_flops = sum(wk[0] for wk in work) * fl_pair
+    stream = torch.cuda.current_stream()
+
+    def run_step(events=None):
+        for r in range(C):
+            uly.forward(r, *bufs[r], events=None if events is None else events[r])
+
+    for _ in range(a.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(C)]
+          for _ in range(a.steps)]
+    for e3 in ev:
+        for e2 in e3:
+            for e in e2:
+                e.record(stream)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(a.steps):
+        run_step(ev[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / a.steps
+    per_rank_ms = [sum(ev[i][r][0].elapsed_time(ev[i][r][1]) for i in range(a.steps)) / a.steps
+                   for r in range(C)]
+    achieved = step_flops / (sum(per_rank_ms) / 1e3) / 1e12
+    kname = L.ra_forward_kernel(uly.local_desc(0, causal=True), L.PART_ALL)
+    res = {
+        "metric": "effective attention TFLOP/s per Ulysses rank-share (bf16), 1 GPU",
+        "value": round(step_flops / (ms_step / 1e3) / 1e12, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)*%g, bf16 RNE)" % w.mult,
+        "config": {"workload": f"{w.name}: causal attention, S={w.seqlen}, Ulysses CP={C} (all "
+                               f"{C} rank shares, each all tokens x {w.hq // C} q heads / "
+                               f"{w.hkv // C} kv heads), head dim {w.dqk}/{w.dv}",
+                   "step_effective_tflop": round(step_flops / 1e12, 4)},
+        "roofline": {"bound": "mfma", "kernel": kname + " (one causal launch per rank share)",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "per_rank": {"ms": [round(x, 4) for x in per_rank_ms],
+                     "pairs_x_heads": [int(wk[0]) for wk in work],
+                     "tiles_visited": [int(wk[1]) for wk in work],
+                     "tiles_skipped": [int(wk[2]) for wk in work]},
+        "cpu_baseline": None,
+    }
+    return res
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -228,6 +291,13 @@ def main():
     k = synth.cast(w.k(), w.dtype).to(dev)
     v = synth.cast(w.v(), w.dtype).to(dev)
     prob = RingProblem(q, k, v, w.cu_global(), w.cp)
+    if a.mode == "ulysses":
+        res = bench_ulysses(a, w, q, k, v, torch, L)
+        ring_work = [prob.work(r) for r in range(w.cp)]
+        res["per_rank"]["ring_pairs_x_heads"] = [int(sum(p for p, _, _ in rw)) for rw in ring_work]
+        res["per_rank"]["ring_tiles_visited"] = [int(sum(t for _, t, _ in rw)) for rw in ring_work]
+        print(json.dumps(res), flush=True)
+        return
     del q, k, v
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

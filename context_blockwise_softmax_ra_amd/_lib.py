@@ -210,8 +210,9 @@ def attn_desc(q, k, v, cu_q, cu_k, cu_q_host, cu_k_host, *, q_part=PART_ALL,
 
 def rank_desc(local: AttnDesc, cp_size: int, rank: int, k_blocks: Sequence, v_blocks: Sequence,
               out, lse, workspace=None, fuse_merge=False, events=None) -> RankDesc:
-    kb = (c_void_p * cp_size)(*[_ptr(t) for t in k_blocks])
-    vb = (c_void_p * cp_size)(*[_ptr(t) for t in v_blocks])
+    # blocks take the local descriptor's token strides (head slices allowed)
+    kb = (c_void_p * cp_size)(*[_ptr(t, True) for t in k_blocks])
+    vb = (c_void_p * cp_size)(*[_ptr(t, True) for t in v_blocks])
     r = RankDesc()
     r.local = local
     r.cp_size, r.rank = cp_size, rank
@@ -236,8 +237,9 @@ def rank_desc(local: AttnDesc, cp_size: int, rank: int, k_blocks: Sequence, v_bl
 
 def rank_bwd_desc(local: AttnDesc, cp_size: int, rank: int, k_blocks, v_blocks, out, dout, lse,
                   dq, dk_blocks, dv_blocks, workspace=None, events=None) -> RankBwdDesc:
-    kb = (c_void_p * cp_size)(*[_ptr(t) for t in k_blocks])
-    vb = (c_void_p * cp_size)(*[_ptr(t) for t in v_blocks])
+    # blocks take the local descriptor's token strides (head slices allowed)
+    kb = (c_void_p * cp_size)(*[_ptr(t, True) for t in k_blocks])
+    vb = (c_void_p * cp_size)(*[_ptr(t, True) for t in v_blocks])
     gk = (c_void_p * cp_size)(*[_ptr(t) for t in dk_blocks])
     gv = (c_void_p * cp_size)(*[_ptr(t) for t in dv_blocks])
     r = RankBwdDesc()

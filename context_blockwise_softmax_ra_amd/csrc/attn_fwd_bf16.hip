@@ -37,7 +37,9 @@
 // Blocks are remapped so that each of the 8 XCDs gets a contiguous range of
 // tiles ordered (segment, kv head, query tile, head in group): the query
 // heads sharing a kv head, and neighbouring query tiles, read the same K/V
-// through the same L2.  Causal launches order query tiles heaviest first.
+// through the same L2.  Causal launches order query tiles heaviest first and
+// deal (query tile x kv group) units round-robin over the XCDs instead, so
+// that every XCD gets light and heavy tiles.
 
 #include "fwd_tiles.h"
 
@@ -70,8 +72,11 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
   __shared__ __attribute__((aligned(1024))) char smem1[G::STAGE];
 
   const int nb = gridDim.x;
-  int b = xcd_remap(blockIdx.x, nb);
   const int group = a.group;
+  // causal work only (one causal block, or a rank share of one block):
+  // deal query tiles over the XCDs; otherwise contiguous ranges per XCD
+  const bool causal_only = MODE == 1 || (MODE == 2 && rk.cp == 1);
+  int b = causal_only ? xcd_deal(blockIdx.x, nb, group) : xcd_remap(blockIdx.x, nb);
   const int hg = b % group;
   b /= group;
   const int qt_rev = b % a.n_qtiles;

@@ -81,6 +81,20 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
   return x * q + (x < r ? x : r) + (b >> 3);
 }
 
+// Causal launches: query tiles differ in work (later rows see more keys), so
+// contiguous ranges per XCD would leave one XCD with all the heavy tiles.
+// Deal units of g consecutive logical tiles (the query heads of one kv
+// group, which read the same K/V) round-robin over the 8 XCDs instead; each
+// XCD then runs light and heavy units alike, in logical (heaviest-first)
+// order.  The last partial round of 8*g blocks keeps the identity.
+__device__ __forceinline__ int xcd_deal(int b, int nb, int g) {
+  const int round = 8 * g;
+  const int full = nb / round * round;
+  if (b >= full) return b;
+  const int x = b & 7, j = b >> 3;
+  return (j / g) * round + x * g + (j % g);
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group,
 // lane i receives element i%4 of the 8 bytes addressed by lane 4r + i/4,
 // r = 0..3.

@@ -178,7 +178,12 @@ ra_status ra_cast_f32_bf16(const float* src, void* dst, int64_t n, void* stream)
  *   j > rank   : non-causal, SECOND half of the rows x all the owner's keys
  * (derived from the global causal rule and the zig-zag placement; the
  * other quarter of each history block is entirely masked and is skipped).
- * k_blocks / v_blocks: host arrays [cp_size] of device pointers, by owner.
+ * k_blocks / v_blocks: host arrays [cp_size] of device pointers, by owner;
+ * every block uses the token strides of `local` (k_stride_tok,
+ * v_stride_tok), so a block may be a head slice of a wider buffer.  With
+ * cp_size = 1 the share is the single causal block: one rank's Ulysses
+ * share (all tokens, a subset of the heads) is ra_rank_forward with
+ * cp_size = 1 over a head slice.
  * out [total_q, hq, dv] of out_dtype, lse [hq, total_q] float32: final.
  * fuse_merge = 0: each step writes a partial to the workspace and
  * ra_lse_merge folds it; 1: steps merge in the attention epilogue;
