@@ -30,6 +30,9 @@ Sources (pages of the subject, cited by title and section):
     blocks are fully visible and use a non-causal call).
   * "Ulysses vs Ring Attention" (iqiancheng), section 1.1 (KV blocks move
     device 0 -> 1 -> ... -> C-1 -> 0).
+  * The oh-bug correctness section on causal rank imbalance also names the
+    other placements implemented in ``map_local_tokens`` (striped /
+    interleaved tokens, contiguous ranges, and the zig-zag mapping).
 
 Readings where the pages are silent or garbled are listed with each function.
 Parity status: every function here is pinned by tests/test_oracle_pins.py.
@@ -321,6 +324,97 @@ def step_coverage(cu_seqlens_global, cp_size: int, rank: int, step: int):
     km = vis.any(axis=0)
     ix = np.ix_(rm, km)
     return rm, km, bool(np.array_equal(vis[ix], same[ix]))
+
+
+# ---------------------------------------------------------------------------
+# Other shard maps (oh-bug, correctness section on causal rank imbalance)
+# ---------------------------------------------------------------------------
+
+SHARD_MAPS = ("zigzag", "zigzag_global", "striped", "contiguous")
+
+
+def map_local_tokens(kind: str, cp_size: int, rank: int,
+                     cu_seqlens_global: Sequence[int]) -> np.ndarray:
+    """Global token of every local row of ``rank`` under a shard map.
+
+    * ``zigzag``: the per-document zig-zag of ``zigzag_local_tokens``.
+    * ``zigzag_global``: the zig-zag applied to the packed stream as if it
+      were one sequence: the T tokens are cut into 2C equal chunks regardless
+      of document boundaries and the rank takes chunks r and 2C-1-r.  This is
+      the mapping the oh-bug page warns about for packed varlen batches
+      (static balance breaks once documents differ in length).
+    * ``striped``: token t of the packed stream goes to rank t mod C (the
+      interleaved / striped placement the oh-bug page lists as a remedy).
+    * ``contiguous``: rank r holds tokens [r T/C, (r+1) T/C), the plain split
+      whose causal imbalance the oh-bug page describes.
+    Every map keeps a rank's tokens in global order.  T must divide by 2C
+    (zigzag_global) or C (striped, contiguous).
+    """
+    cu = np.asarray(cu_seqlens_global, dtype=np.int64)
+    T = int(cu[-1])
+    C = cp_size
+    if not (0 <= rank < C):
+        raise ValueError("rank out of range")
+    if kind == "zigzag":
+        return zigzag_local_tokens(C, rank, cu)[0]
+    if kind == "zigzag_global":
+        if T % (2 * C):
+            raise ValueError("stream length not divisible by 2*C")
+        c = T // (2 * C)
+        a, b = zigzag_chunks(C, rank)
+        return np.concatenate([np.arange(a * c, (a + 1) * c), np.arange(b * c, (b + 1) * c)])
+    if kind == "striped":
+        if T % C:
+            raise ValueError("stream length not divisible by C")
+        return np.arange(rank, T, C, dtype=np.int64)
+    if kind == "contiguous":
+        if T % C:
+            raise ValueError("stream length not divisible by C")
+        L = T // C
+        return np.arange(rank * L, (rank + 1) * L, dtype=np.int64)
+    raise ValueError(f"unknown shard map {kind}")
+
+
+def rank_share_map(kind: str, q_glob, k_glob, v_glob, cu_seqlens_global, cp_size: int,
+                   rank: int, scale: Optional[float] = None):
+    """``rank_share`` for any shard map: the rank's rows against every owner's
+    keys in ring order (owner (r - s) mod C at step s), under the global
+    document-causal rule, partials folded with ``lse_merge``."""
+    lay = Layout(cu_seqlens_global)
+    rows = map_local_tokens(kind, cp_size, rank, lay.cu)
+    q = np.asarray(q_glob)[rows]
+    out_acc = lse_acc = None
+    steps = []
+    for s in range(cp_size):
+        owner = ring_owner(rank, s, cp_size)
+        krows = map_local_tokens(kind, cp_size, owner, lay.cu)
+        o, l = attention(q, np.asarray(k_glob)[krows], np.asarray(v_glob)[krows],
+                         lay.pos[rows], lay.doc[rows], lay.pos[krows], lay.doc[krows],
+                         scale=scale, causal=True)
+        steps.append((owner, o, l))
+        if out_acc is None:
+            out_acc, lse_acc = o, l
+        else:
+            out_acc, lse_acc = lse_merge(out_acc, lse_acc, o, l)
+    return {"rows": rows, "out": out_acc, "lse": lse_acc, "steps": steps}
+
+
+def map_visible_pairs(kind: str, cu_seqlens_global, cp_size: int, rank: int) -> int:
+    """(query, key) pairs a rank's rows see under a shard map (per query head):
+    every row sees the keys of its document up to itself."""
+    lay = Layout(cu_seqlens_global)
+    rows = map_local_tokens(kind, cp_size, rank, lay.cu)
+    return int((rows - lay.cu[lay.doc[rows]] + 1).sum())
+
+
+def step_visible(kind: str, cu_seqlens_global, cp_size: int, rank: int,
+                 owner: int) -> np.ndarray:
+    """Boolean [rank's local rows, owner's local keys]: which pairs are
+    visible when ``rank`` holds ``owner``'s KV block (small inputs only)."""
+    lay = Layout(cu_seqlens_global)
+    rows = map_local_tokens(kind, cp_size, rank, lay.cu)
+    keys = map_local_tokens(kind, cp_size, owner, lay.cu)
+    return _visible(lay.pos[rows], lay.doc[rows], lay.pos[keys], lay.doc[keys], True)
 
 
 # ---------------------------------------------------------------------------

@@ -474,6 +474,90 @@ def test_bf16_rounding_vs_torch_cast():
 # planted mistakes must be caught
 # ---------------------------------------------------------------------------
 
+# ---------------------------------------------------------------------------
+# other shard maps (oh-bug correctness section on causal imbalance)
+# ---------------------------------------------------------------------------
+
+def test_shard_maps_hand_examples():
+    cu = [0, 8]
+    assert list(oracle.map_local_tokens("striped", 2, 0, cu)) == [0, 2, 4, 6]
+    assert list(oracle.map_local_tokens("striped", 2, 1, cu)) == [1, 3, 5, 7]
+    assert list(oracle.map_local_tokens("contiguous", 2, 0, cu)) == [0, 1, 2, 3]
+    assert list(oracle.map_local_tokens("contiguous", 2, 1, cu)) == [4, 5, 6, 7]
+    assert list(oracle.map_local_tokens("zigzag_global", 2, 0, cu)) == [0, 1, 6, 7]
+    assert list(oracle.map_local_tokens("zigzag_global", 2, 1, cu)) == [2, 3, 4, 5]
+    # documents [0,4) and [4,8): the stream-level zig-zag ignores the boundary,
+    # the per-document one splits each document
+    assert list(oracle.map_local_tokens("zigzag_global", 2, 0, [0, 4, 8])) == [0, 1, 6, 7]
+    assert list(oracle.map_local_tokens("zigzag", 2, 0, [0, 4, 8])) == [0, 3, 4, 7]
+
+
+@pytest.mark.parametrize("kind", oracle.SHARD_MAPS)
+@pytest.mark.parametrize("lengths,C", [([64], 4), ([16, 48, 8, 56], 4), ([32, 96], 8)])
+def test_shard_maps_partition_the_stream(kind, lengths, C):
+    cu = synth.cu_seqlens(lengths)
+    T = int(cu[-1])
+    parts = [oracle.map_local_tokens(kind, C, r, cu) for r in range(C)]
+    for p in parts:
+        assert len(p) == T // C and np.all(np.diff(p) > 0)    # equal shares, global order
+    assert np.array_equal(np.sort(np.concatenate(parts)), np.arange(T))
+
+
+def test_single_sequence_stream_zigzag_is_the_zigzag():
+    for r in range(4):
+        assert np.array_equal(oracle.map_local_tokens("zigzag_global", 4, r, [0, 128]),
+                              oracle.map_local_tokens("zigzag", 4, r, [0, 128]))
+
+
+@pytest.mark.parametrize("kind", oracle.SHARD_MAPS)
+def test_concat_of_map_rank_shares_equals_full_attention(kind):
+    lengths, C, hq, hkv, d = [16, 48, 8, 56], 4, 2, 1, 8
+    cu = synth.cu_seqlens(lengths)
+    T = int(cu[-1])
+    q, k, v = _rand(T, hq, d), _rand(T, hkv, d), _rand(T, hkv, d)
+    full_o, full_l = oracle.full_attention(q, k, v, cu)
+    cat_o = np.full_like(full_o, np.nan)
+    cat_l = np.full_like(full_l, np.nan)
+    for r in range(C):
+        res = oracle.rank_share_map(kind, q, k, v, cu, C, r)
+        cat_o[res["rows"]] = res["out"]
+        cat_l[:, res["rows"]] = res["lse"]
+    assert np.abs(cat_o - full_o).max() <= 1e-12
+    assert np.abs(cat_l - full_l).max() <= 1e-12
+
+
+def test_map_pair_counts_closed_forms_and_imbalance():
+    S, C = 256, 4
+    L = S // C
+    cu = [0, S]
+    for r in range(C):
+        # contiguous: rows rL .. rL+L-1 see t+1 keys each
+        assert oracle.map_visible_pairs("contiguous", cu, C, r) == L * (2 * r * L + L + 1) // 2
+        # striped: rows iC + r, i < L
+        assert oracle.map_visible_pairs("striped", cu, C, r) == C * L * (L - 1) // 2 + L * (r + 1)
+        # both zig-zags balance one sequence exactly: (S^2 + S) / (2C)
+        for kind in ("zigzag", "zigzag_global"):
+            assert oracle.map_visible_pairs(kind, cu, C, r) == (S * S + S) // (2 * C)
+    lengths = [16, 48, 8, 56, 8, 120]
+    cu = synth.cu_seqlens(lengths)
+    total = sum(l * (l + 1) // 2 for l in lengths)
+    for kind in oracle.SHARD_MAPS:
+        per = [oracle.map_visible_pairs(kind, cu, 4, r) for r in range(4)]
+        assert sum(per) == total, kind
+        if kind == "zigzag":
+            assert len(set(per)) == 1
+        if kind == "zigzag_global":
+            assert len(set(per)) > 1           # the packed-varlen imbalance
+
+
+@pytest.mark.parametrize("kind", oracle.SHARD_MAPS)
+def test_step_visibility_sums_to_rank_pairs(kind):
+    cu = synth.cu_seqlens([16, 48, 8, 56])
+    for r in range(4):
+        tot = sum(int(oracle.step_visible(kind, cu, 4, r, o).sum()) for o in range(4))
+        assert tot == oracle.map_visible_pairs(kind, cu, 4, r)
+
+
 def _pins_pass():
     """Run a representative subset of the pins; False if any fails."""
     try:
@@ -485,6 +569,9 @@ def _pins_pass():
         test_merge_formula_on_printed_lse_rule_and_large_values()
         test_backward_sum_rules()
         test_step_coverage_matches_part_plan()
+        test_shard_maps_hand_examples()
+        test_concat_of_map_rank_shares_equals_full_attention("striped")
+        test_map_pair_counts_closed_forms_and_imbalance()
     except (AssertionError, ValueError, FloatingPointError):
         return False
     return True
@@ -498,6 +585,10 @@ MUTANTS = {
                           (kp[None, :] <= qp[:, None]) if causal else np.ones((len(qp), len(kp)), bool)),
     "zigzag_off_by_one": ("zigzag_chunks", lambda c, r: (r, 2 * c - 2 - r) if r < c - 1 else (r, c)),
     "scale_wrong": ("softmax_scale", lambda d: 1.0 / d),
+    # a relabelling of ranks still partitions the stream; only the printed /
+    # hand examples and closed forms catch it
+    "striped_ranks_rotated": ("map_local_tokens", lambda kind, C, r, cu, _f=ref.map_local_tokens:
+                              _f(kind, C, (r + 1) % C if kind == "striped" else r, cu)),
 }
 
 
