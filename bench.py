@@ -48,6 +48,11 @@ def parse():
                     help="ring: zig-zag ring-attention rank shares (the headline); ulysses: "
                          "the Ulysses rank shares of the same workload (all tokens, Hq/C "
                          "heads each) on the same kernels, with the per-rank work of both")
+    ap.add_argument("--map", default=None,
+                    choices=("zigzag", "zigzag_global", "striped", "contiguous"),
+                    help="run the ring shares under this shard map through per-step rectangle "
+                         "launches (the same 4-wave kernel for every map) and report the "
+                         "per-rank work and time imbalance")
     ap.add_argument("--kernel", default="auto", choices=("auto", "4w", "pp"),
                     help="bf16 forward kernel: chosen by launch size (auto), the 4-wave "
                          "kernel, or the 8-wave ping-pong kernel")
@@ -263,6 +268,71 @@ def bench_ulysses(a, w, q, k, v, torch, L):
     return res
 
 
+def bench_map(a, w, q, k, v, torch, L):
+    """Forward step under a shard map: every rank's share as C rectangle launches."""
+    from context_blockwise_softmax_ra_amd.maps import MapProblem
+    C = w.cp
+    prob = MapProblem(a.map, q, k, v, w.cu_global(), C)
+    bufs = [prob.alloc_forward() for _ in range(C)]
+    fl_pair = 2 * (w.dqk + w.dv)
+    work = [prob.work(r) for r in range(C)]
+    rank_pairs = [sum(p for p, _, _ in wk) for wk in work]
+    step_flops = sum(rank_pairs) * fl_pair
+    stream = torch.cuda.current_stream()
+
+    def run_step(events=None):
+        for r in range(C):
+            prob.forward(r, *bufs[r], events=None if events is None else events[r])
+
+    for _ in range(a.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2 * C)] for _ in range(C)]
+          for _ in range(a.steps)]
+    for e3 in ev:
+        for e2 in e3:
+            for e in e2:
+                e.record(stream)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(a.steps):
+        run_step(ev[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / a.steps
+    rank_ms = [sum(ev[i][r][2 * s].elapsed_time(ev[i][r][2 * s + 1])
+                   for i in range(a.steps) for s in range(C)) / a.steps for r in range(C)]
+    achieved = step_flops / (sum(rank_ms) / 1e3) / 1e12
+    mean_ms = sum(rank_ms) / C
+    mean_pairs = sum(rank_pairs) / C
+    slow = max(range(C), key=lambda r: rank_ms[r])
+    return {
+        "metric": "effective attention TFLOP/s per rank-share (bf16) under a shard map, 1 GPU",
+        "value": round(step_flops / (ms_step / 1e3) / 1e12, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)*%g, bf16 RNE)" % w.mult,
+        "config": {"workload": f"{w.name}: causal attention, S={w.seqlen}, CP={C}, shard map "
+                               f"{a.map} (all {C} rank shares, each C rectangle launches merged "
+                               f"in the epilogue), {w.hq} q heads / {w.hkv} kv heads, head dim "
+                               f"{w.dqk}/{w.dv}",
+                   "map": a.map, "step_effective_tflop": round(step_flops / 1e12, 4)},
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16 (rectangle lists)",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "per_rank": {"ms": [round(x, 4) for x in rank_ms],
+                     "pairs_x_heads": [int(x) for x in rank_pairs],
+                     "tiles_visited": [int(sum(t for _, t, _ in wk)) for wk in work],
+                     "slowest_rank": slow,
+                     "time_max_over_mean": round(rank_ms[slow] / mean_ms, 4),
+                     "pairs_max_over_mean": round(max(rank_pairs) / mean_pairs, 4),
+                     "concurrent_step_ms": round(rank_ms[slow], 4)},
+        "cpu_baseline": None,
+    }
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -291,6 +361,10 @@ def main():
     k = synth.cast(w.k(), w.dtype).to(dev)
     v = synth.cast(w.v(), w.dtype).to(dev)
     prob = RingProblem(q, k, v, w.cu_global(), w.cp)
+    if a.map is not None:
+        res = bench_map(a, w, q, k, v, torch, L)
+        print(json.dumps(res), flush=True)
+        return
     if a.mode == "ulysses":
         res = bench_ulysses(a, w, q, k, v, torch, L)
         ring_work = [prob.work(r) for r in range(w.cp)]
@@ -349,10 +423,12 @@ def main():
     diag_ms = hist_ms = 0.0
     diag_fl = hist_fl = 0.0
     n_launch = 0
+    rank_ms = [0.0] * C
     for i in range(a.steps):
         for r in range(C):
             if a.fuse_merge == 2:                                # one launch per rank share
                 d = ev[i][r][0].elapsed_time(ev[i][r][1])
+                rank_ms[r] += d / a.steps
                 attn_ms += d
                 attn_flops += sum(p for (p, _, _) in work[r]) * fl_pair
                 n_launch += 1
@@ -360,6 +436,7 @@ def main():
             for s in range(C):
                 d = ev[i][r][2 * s].elapsed_time(ev[i][r][2 * s + 1])
                 f = work[r][s][0] * fl_pair
+                rank_ms[r] += d / a.steps
                 attn_ms += d
                 attn_flops += f
                 n_launch += 1
@@ -414,6 +491,12 @@ def main():
             "launches": n_launch,
             "diag_tflops": round(diag_fl / (diag_ms / 1e3) / 1e12, 2) if diag_ms else None,
             "history_tflops": round(hist_fl / (hist_ms / 1e3) / 1e12, 2) if hist_ms else None,
+        },
+        "per_rank": {
+            "ms": [round(x, 4) for x in rank_ms],
+            "pairs_x_heads": [int(sum(p for (p, _, _) in work[r])) for r in range(C)],
+            "slowest_rank": max(range(C), key=lambda r: rank_ms[r]),
+            "time_max_over_mean": round(max(rank_ms) / (sum(rank_ms) / C), 4),
         },
         "cpu_baseline": None,
     }

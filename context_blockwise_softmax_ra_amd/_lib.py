@@ -28,8 +28,13 @@ EXPORTS = (
     "ra_block_attn_fwd", "ra_block_attn_fwd_merge", "ra_lse_merge", "ra_zigzag_shard_map",
     "ra_zigzag_gather", "ra_zigzag_scatter", "ra_cast_f32_bf16", "ra_rank_forward_workspace",
     "ra_rank_forward", "ra_attn_bwd_delta", "ra_block_attn_bwd", "ra_rank_backward_workspace",
-    "ra_rank_backward", "ra_block_attn_work", "ra_forward_kernel", "ra_last_error", "ra_version",
+    "ra_rank_backward", "ra_block_attn_work", "ra_forward_kernel", "ra_shard_tokens",
+    "ra_step_segments", "ra_gather_tokens", "ra_scatter_tokens", "ra_block_attn_fwd_segments",
+    "ra_segments_work", "ra_last_error", "ra_version",
 )
+
+# ra_map values by name (the oracle's names for the same placements)
+MAPS = {"zigzag": 0, "zigzag_global": 1, "striped": 2, "contiguous": 3}
 
 
 class RaError(RuntimeError):
@@ -111,6 +116,14 @@ def lib():
             "ra_rank_backward": [POINTER(RankBwdDesc), vp],
             "ra_block_attn_work": [POINTER(AttnDesc), POINTER(c_int64), POINTER(c_int64),
                                    POINTER(c_int64)],
+            "ra_shard_tokens": [c_int, c_int32, c_int32, c_int32, vp, vp, c_int32, vp],
+            "ra_step_segments": [c_int, c_int32, c_int32, c_int32, c_int32, vp, vp, c_int32, vp],
+            "ra_gather_tokens": [vp, vp, c_int64, c_int32, vp, vp, c_int32, vp],
+            "ra_scatter_tokens": [vp, vp, c_int64, c_int32, vp, vp, c_int32, vp],
+            "ra_block_attn_fwd_segments": [POINTER(AttnDesc), c_int32, vp, vp, vp, vp, c_int32,
+                                           vp],
+            "ra_segments_work": [vp, c_int32, c_int32, POINTER(c_int64), POINTER(c_int64),
+                                 POINTER(c_int64)],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -357,6 +370,65 @@ def ra_block_attn_work(desc: AttnDesc):
     a, b, c = c_int64(0), c_int64(0), c_int64(0)
     _check(lib().ra_block_attn_work(ctypes.byref(desc), ctypes.byref(a), ctypes.byref(b),
                                     ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+def _map_code(kind) -> int:
+    return MAPS[kind] if isinstance(kind, str) else int(kind)
+
+
+def ra_shard_tokens(kind, cp_size: int, rank: int, cu_seqlens_global) -> np.ndarray:
+    """Global token of each local row of ``rank`` under a shard map (int32)."""
+    cu = _host_i32(cu_seqlens_global)
+    cap = max(int(cu[-1]) // max(cp_size, 1), 1)
+    out = np.zeros(cap, np.int32)
+    n = c_int32(0)
+    _check(lib().ra_shard_tokens(_map_code(kind), cp_size, rank, len(cu) - 1, cu.ctypes.data,
+                                 out.ctypes.data, cap, ctypes.byref(n)))
+    return out[:n.value].copy()
+
+
+def ra_step_segments(kind, cp_size: int, rank: int, owner: int, cu_seqlens_global) -> np.ndarray:
+    """Rectangles [n, 5] int32 (q_lo, q_hi, k_lo, k_hi, diag) of one ring step."""
+    cu = _host_i32(cu_seqlens_global)
+    cap = 2 * (len(cu) - 1) + 2
+    out = np.zeros((cap, 5), np.int32)
+    n = c_int32(0)
+    _check(lib().ra_step_segments(_map_code(kind), cp_size, rank, owner, len(cu) - 1,
+                                  cu.ctypes.data, out.ctypes.data, cap, ctypes.byref(n)))
+    return out[:n.value].copy()
+
+
+def ra_gather_tokens(src, dst, tokens_dev, tokens_host, stream=None):
+    """dst[i] = src[tokens[i]] for [T, ...] row buffers."""
+    th = np.ascontiguousarray(tokens_host, np.int32)
+    rb = src[0].numel() * src.element_size()
+    _check(lib().ra_gather_tokens(_ptr(src), _ptr(dst), rb, src.shape[0], _ptr(tokens_dev),
+                                  th.ctypes.data, len(th), _stream(stream)))
+
+
+def ra_scatter_tokens(src, dst, tokens_dev, tokens_host, stream=None):
+    """dst[tokens[i]] = src[i] for [T, ...] row buffers."""
+    th = np.ascontiguousarray(tokens_host, np.int32)
+    rb = src[0].numel() * src.element_size()
+    _check(lib().ra_scatter_tokens(_ptr(src), _ptr(dst), rb, dst.shape[0], _ptr(tokens_dev),
+                                   th.ctypes.data, len(th), _stream(stream)))
+
+
+def ra_block_attn_fwd_segments(desc: AttnDesc, segs_dev, segs_host, out, lse, merge=False,
+                               stream=None):
+    sh = np.ascontiguousarray(segs_host, np.int32).reshape(-1, 5)
+    _check(lib().ra_block_attn_fwd_segments(ctypes.byref(desc), len(sh), _ptr(segs_dev),
+                                            sh.ctypes.data, _ptr(out), _ptr(lse), 1 if merge else 0,
+                                            _stream(stream)))
+
+
+def ra_segments_work(segs_host, hq: int):
+    """(visible_pairs, tiles_visited, tiles_skipped) of a rectangle list."""
+    sh = np.ascontiguousarray(segs_host, np.int32).reshape(-1, 5)
+    a, b, c = c_int64(0), c_int64(0), c_int64(0)
+    _check(lib().ra_segments_work(sh.ctypes.data, len(sh), hq, ctypes.byref(a), ctypes.byref(b),
+                                  ctypes.byref(c)))
     return a.value, b.value, c.value
 
 

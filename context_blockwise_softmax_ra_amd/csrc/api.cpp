@@ -9,8 +9,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <climits>
 #include <cstring>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "ra_internal.h"
@@ -274,6 +276,133 @@ ra_status check_rank_common(const ra_attn_desc& L, int cp, int rank, const void*
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---------------------------------------------------------------------------
+// Other shard maps: token lists and the rectangles of one ring step
+// ---------------------------------------------------------------------------
+
+// Consecutive global tokens of a rank, at consecutive local rows.
+struct Run {
+  int64_t local_lo, global_lo, len;
+  int doc;
+};
+
+ra_status check_map(ra_map kind, int cp, int rank, int n_seq, const int32_t* cu) {
+  if (kind < RA_MAP_ZIGZAG || kind > RA_MAP_CONTIGUOUS)
+    return fail(RA_ERR_INVALID_ARG, "unknown shard map %d", (int)kind);
+  if (cp <= 0 || rank < 0 || rank >= cp)
+    return fail(RA_ERR_INVALID_ARG, "bad cp_size %d / rank %d", cp, rank);
+  if (n_seq <= 0) return fail(RA_ERR_INVALID_ARG, "n_seq must be >= 1");
+  ra_status st = check_cu(cu, n_seq, "cu_seqlens_global");
+  if (st != RA_OK) return st;
+  if (cu[0] != 0) return fail(RA_ERR_INVALID_ARG, "cu_seqlens_global must start at 0");
+  const int64_t T = cu[n_seq];
+  if (kind == RA_MAP_ZIGZAG) {
+    for (int d = 0; d < n_seq; ++d)
+      if ((cu[d + 1] - cu[d]) % (2 * cp))
+        return fail(RA_ERR_INVALID_ARG, "sequence %d length is not a multiple of 2*cp_size", d);
+  } else if (kind == RA_MAP_ZIGZAG_GLOBAL) {
+    if (T % (2 * cp)) return fail(RA_ERR_INVALID_ARG, "stream length not a multiple of 2*cp_size");
+  } else if (T % cp) {
+    return fail(RA_ERR_INVALID_ARG, "stream length not a multiple of cp_size");
+  }
+  return RA_OK;
+}
+
+// Runs of a rank's tokens (all maps but the striped one), split at document
+// boundaries, in local order.
+std::vector<Run> rank_runs(ra_map kind, int cp, int r, int n_seq, const int32_t* cu) {
+  std::vector<Run> runs;
+  const int64_t T = cu[n_seq];
+  if (kind == RA_MAP_ZIGZAG) {
+    int64_t local = 0;
+    for (int d = 0; d < n_seq; ++d) {
+      const int64_t c = (cu[d + 1] - cu[d]) / (2 * cp);
+      if (c == 0) continue;
+      runs.push_back({local, cu[d] + (int64_t)r * c, c, d});
+      runs.push_back({local + c, cu[d] + (int64_t)(2 * cp - 1 - r) * c, c, d});
+      local += 2 * c;
+    }
+    return runs;
+  }
+  std::vector<Run> raw;
+  if (kind == RA_MAP_ZIGZAG_GLOBAL) {
+    const int64_t c = T / (2 * cp);
+    raw.push_back({0, (int64_t)r * c, c, 0});
+    raw.push_back({c, (int64_t)(2 * cp - 1 - r) * c, c, 0});
+  } else {
+    const int64_t L = T / cp;
+    raw.push_back({0, (int64_t)r * L, L, 0});
+  }
+  for (const Run& x : raw) {
+    int64_t g = x.global_lo;
+    const int64_t end = x.global_lo + x.len;
+    int d = (int)(std::upper_bound(cu, cu + n_seq + 1, (int32_t)g) - cu) - 1;
+    while (g < end && d < n_seq) {
+      const int64_t e = std::min<int64_t>(end, cu[d + 1]);
+      if (e > g) runs.push_back({x.local_lo + (g - x.global_lo), g, e - g, d});
+      g = std::max<int64_t>(g, e);
+      ++d;
+    }
+  }
+  return runs;
+}
+
+int64_t ceil_pos(int64_t a, int64_t c) { return a <= 0 ? 0 : (a + c - 1) / c; }
+
+ra_status step_segments(ra_map kind, int cp, int r, int o, int n_seq, const int32_t* cu,
+                        std::vector<ra_segment>* out) {
+  out->clear();
+  auto push = [&](int64_t q_lo, int64_t q_hi, int64_t k_lo, int64_t k_hi, int64_t diag) {
+    const int64_t klen = k_hi - k_lo;
+    if (q_hi <= q_lo || klen <= 0) return;
+    if ((q_hi - q_lo - 1) + diag < 0) return;  // no row sees a key
+    if (diag >= klen - 1) diag = klen;         // every key visible
+    out->push_back({(int32_t)q_lo, (int32_t)q_hi, (int32_t)k_lo, (int32_t)k_hi, (int32_t)diag});
+  };
+  if (kind == RA_MAP_STRIPED) {
+    // local row i of rank r is token i*cp + r: key j of owner o is not after
+    // row i iff j <= i (o <= r) or j <= i - 1 (o > r)
+    const int off = o <= r ? 0 : -1;
+    for (int d = 0; d < n_seq; ++d) {
+      const int64_t qa = ceil_pos(cu[d] - r, cp), qb = ceil_pos(cu[d + 1] - r, cp);
+      const int64_t ka = ceil_pos(cu[d] - o, cp), kb = ceil_pos(cu[d + 1] - o, cp);
+      push(qa, qb, ka, kb, qa - ka + off);
+    }
+    return RA_OK;
+  }
+  const std::vector<Run> qr = rank_runs(kind, cp, r, n_seq, cu);
+  const std::vector<Run> kr = rank_runs(kind, cp, o, n_seq, cu);
+  std::vector<std::vector<int>> by_doc(n_seq);
+  for (int i = 0; i < (int)kr.size(); ++i) by_doc[kr[i].doc].push_back(i);
+  for (const Run& p : qr) {
+    // key runs of the same document that some row of p can see: all keys
+    // before p's first token (full), or overlapping p's range (causal with
+    // the offset of their global starts); merged into one rectangle
+    int64_t k_lo = -1, k_hi = -1, diag = 0;
+    bool full = true;
+    for (int i : by_doc[p.doc]) {
+      const Run& k = kr[i];
+      if (k.global_lo > p.global_lo + p.len - 1) continue;  // after every row
+      const bool kfull = k.global_lo + k.len - 1 <= p.global_lo;
+      if (k_lo < 0) {
+        k_lo = k.local_lo;
+      } else if (k.local_lo != k_hi || !full) {
+        return fail(RA_ERR_UNSUPPORTED, "step rectangle of rank %d / owner %d not contiguous", r, o);
+      }
+      if (!kfull) {
+        if (p.global_lo - k.global_lo < -1)
+          return fail(RA_ERR_UNSUPPORTED, "step rectangle of rank %d / owner %d not expressible", r, o);
+        diag = (k.local_lo - k_lo) + (p.global_lo - k.global_lo);
+        full = false;
+      }
+      k_hi = k.local_lo + k.len;
+    }
+    if (k_lo < 0) continue;
+    push(p.local_lo, p.local_lo + p.len, k_lo, k_hi, full ? (k_hi - k_lo) : diag);
+  }
+  return RA_OK;
+}
 
 }  // namespace
 
@@ -671,6 +800,155 @@ ra_status ra_rank_backward(const ra_rank_bwd_desc* d, void* stream) {
         (e = hipEventRecord((hipEvent_t)d->events[2 * s + 1], hs)) != hipSuccess)
       return hip_fail(e, "event record");
   }
+  return ok();
+}
+
+ra_status ra_shard_tokens(ra_map kind, int32_t cp_size, int32_t rank, int32_t n_seq,
+                          const int32_t* cu_seqlens_global, int32_t* tokens, int32_t capacity,
+                          int32_t* n_tokens) {
+  ra_status st = check_map(kind, cp_size, rank, n_seq, cu_seqlens_global);
+  if (st != RA_OK) return st;
+  if (!tokens || !n_tokens) return fail(RA_ERR_INVALID_ARG, "NULL output");
+  const int64_t T = cu_seqlens_global[n_seq], n = T / cp_size;
+  if (capacity < n) return fail(RA_ERR_INVALID_ARG, "capacity %d < %lld tokens", capacity, (long long)n);
+  if (kind == RA_MAP_STRIPED) {
+    for (int64_t i = 0; i < n; ++i) tokens[i] = (int32_t)(i * cp_size + rank);
+  } else {
+    for (const Run& x : rank_runs(kind, cp_size, rank, n_seq, cu_seqlens_global))
+      for (int64_t i = 0; i < x.len; ++i) tokens[x.local_lo + i] = (int32_t)(x.global_lo + i);
+  }
+  *n_tokens = (int32_t)n;
+  return ok();
+}
+
+ra_status ra_step_segments(ra_map kind, int32_t cp_size, int32_t rank, int32_t owner,
+                           int32_t n_seq, const int32_t* cu_seqlens_global, ra_segment* segs,
+                           int32_t capacity, int32_t* n_segs) {
+  ra_status st = check_map(kind, cp_size, rank, n_seq, cu_seqlens_global);
+  if (st != RA_OK) return st;
+  if (owner < 0 || owner >= cp_size) return fail(RA_ERR_INVALID_ARG, "bad owner %d", owner);
+  if (!segs || !n_segs) return fail(RA_ERR_INVALID_ARG, "NULL output");
+  std::vector<ra_segment> v;
+  if ((st = step_segments(kind, cp_size, rank, owner, n_seq, cu_seqlens_global, &v)) != RA_OK)
+    return st;
+  if ((int64_t)v.size() > capacity)
+    return fail(RA_ERR_INVALID_ARG, "capacity %d < %zu rectangles", capacity, v.size());
+  std::copy(v.begin(), v.end(), segs);
+  *n_segs = (int32_t)v.size();
+  return ok();
+}
+
+static ra_status token_copy(const void* src, void* dst, int64_t row_bytes, int32_t n_rows,
+                            const int32_t* tok, const int32_t* tok_host, int32_t n, bool gather,
+                            void* stream) {
+  if (!src || !dst || (n > 0 && (!tok || !tok_host)))
+    return fail(RA_ERR_INVALID_ARG, "NULL argument");
+  if (row_bytes <= 0 || (row_bytes % 16) || !aligned16(src) || !aligned16(dst))
+    return fail(RA_ERR_INVALID_ARG, "rows must be 16-byte multiples and aligned");
+  if (n < 0 || n_rows < 0) return fail(RA_ERR_INVALID_ARG, "negative count");
+  for (int32_t i = 0; i < n; ++i)
+    if (tok_host[i] < 0 || tok_host[i] >= n_rows)
+      return fail(RA_ERR_INVALID_ARG, "token %d of row %d outside [0, %d)", tok_host[i], i, n_rows);
+  hipError_t e = ra::launch_gather_tokens(src, dst, row_bytes, tok, n, gather, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "token copy launch");
+  return ok();
+}
+
+ra_status ra_gather_tokens(const void* src, void* dst, int64_t row_bytes, int32_t n_rows,
+                           const int32_t* tokens_dev, const int32_t* tokens_host, int32_t n,
+                           void* stream) {
+  return token_copy(src, dst, row_bytes, n_rows, tokens_dev, tokens_host, n, true, stream);
+}
+
+ra_status ra_scatter_tokens(const void* src, void* dst, int64_t row_bytes, int32_t n_rows,
+                            const int32_t* tokens_dev, const int32_t* tokens_host, int32_t n,
+                            void* stream) {
+  return token_copy(src, dst, row_bytes, n_rows, tokens_dev, tokens_host, n, false, stream);
+}
+
+static ra_status check_segments(const ra_segment* segs, int32_t n_seg, int64_t Tq, int64_t Tk,
+                                int* max_q) {
+  if (n_seg < 0) return fail(RA_ERR_INVALID_ARG, "negative n_seg");
+  if (n_seg > 0 && !segs) return fail(RA_ERR_INVALID_ARG, "segments are NULL");
+  std::vector<std::pair<int32_t, int32_t>> rows;
+  *max_q = 0;
+  for (int i = 0; i < n_seg; ++i) {
+    const ra_segment& g = segs[i];
+    if (g.q_lo < 0 || g.q_lo > g.q_hi || g.q_hi > Tq || g.k_lo < 0 || g.k_lo > g.k_hi ||
+        g.k_hi > Tk)
+      return fail(RA_ERR_INVALID_ARG, "rectangle %d outside the buffers", i);
+    if (g.diag < -(1 << 30) || g.diag > (1 << 30))
+      return fail(RA_ERR_INVALID_ARG, "rectangle %d: diag out of range", i);
+    if (g.q_hi > g.q_lo) rows.push_back({g.q_lo, g.q_hi});
+    *max_q = std::max(*max_q, g.q_hi - g.q_lo);
+  }
+  std::sort(rows.begin(), rows.end());
+  for (size_t i = 1; i < rows.size(); ++i)
+    if (rows[i].first < rows[i - 1].second)
+      return fail(RA_ERR_INVALID_ARG, "rectangles overlap in rows [%d, %d)", rows[i].first,
+                  rows[i - 1].second);
+  return RA_OK;
+}
+
+ra_status ra_block_attn_fwd_segments(const ra_attn_desc* d, int32_t n_seg,
+                                     const ra_segment* segs_dev, const ra_segment* segs_host,
+                                     float* out, float* lse, int32_t merge, void* stream) {
+  if (!d) return fail(RA_ERR_INVALID_ARG, "descriptor is NULL");
+  if (d->n_seq != 1)
+    return fail(RA_ERR_INVALID_ARG, "rectangle lists take n_seq = 1 (buffer row counts)");
+  ra_attn_desc t = *d;
+  t.causal = 0;
+  t.q_part = RA_PART_ALL;
+  t.k_part = RA_PART_ALL;
+  Checked c;
+  ra_status st = check_desc(&t, true, &c);
+  if (st != RA_OK) return st;
+  if (d->dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "rectangle lists are bf16 only");
+  if (!out || !lse) return fail(RA_ERR_INVALID_ARG, "out or lse is NULL");
+  if (!aligned16(out)) return fail(RA_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  if (n_seg > 0 && !segs_dev) return fail(RA_ERR_INVALID_ARG, "device segments are NULL");
+  int max_q = 0;
+  if ((st = check_segments(segs_host, n_seg, c.total_q, c.total_k, &max_q)) != RA_OK) return st;
+  if (n_seg == 0 || max_q == 0) return ok();
+  ra::AttnArgs a = make_args(&t, c);
+  a.segs = segs_dev;
+  a.n_seq = n_seg;
+  a.n_qtiles = (max_q + ra::kFwdBlockM - 1) / ra::kFwdBlockM;
+  a.out = out;
+  a.lse = lse;
+  hipError_t e = ra::launch_attn_fwd_segments(a, d->dqk, d->dv, merge != 0, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "rectangle attention launch");
+  return ok();
+}
+
+ra_status ra_segments_work(const ra_segment* segs, int32_t n_seg, int32_t hq,
+                           int64_t* visible_pairs, int64_t* tiles_visited, int64_t* tiles_skipped) {
+  if (!visible_pairs || !tiles_visited || !tiles_skipped)
+    return fail(RA_ERR_INVALID_ARG, "NULL output");
+  if (hq <= 0) return fail(RA_ERR_INVALID_ARG, "hq must be >= 1");
+  int max_q = 0;
+  ra_status st = check_segments(segs, n_seg, INT32_MAX, INT32_MAX, &max_q);
+  if (st != RA_OK) return st;
+  const int bm = ra::kFwdBlockM, bn = ra::kFwdBlockN;
+  int64_t pairs = 0, vis = 0, skip = 0;
+  for (int i = 0; i < n_seg; ++i) {
+    const ra_segment& g = segs[i];
+    const int64_t lq = g.q_hi - g.q_lo, lk = g.k_hi - g.k_lo;
+    const bool full = g.diag >= lk;
+    for (int64_t r = 0; r < lq; ++r)
+      pairs += full ? lk : std::min<int64_t>(lk, std::max<int64_t>(0, r + g.diag + 1));
+    const int64_t all_tiles = (lk + bn - 1) / bn;
+    for (int64_t q0 = 0; q0 < lq; q0 += bm) {
+      const int64_t last = std::min<int64_t>(q0 + bm, lq) - 1;
+      const int64_t kend = full ? lk : std::min<int64_t>(lk, std::max<int64_t>(0, last + g.diag + 1));
+      const int64_t v = (kend + bn - 1) / bn;
+      vis += v;
+      skip += all_tiles - v;
+    }
+  }
+  *visible_pairs = pairs * hq;
+  *tiles_visited = vis * hq;
+  *tiles_skipped = skip * hq;
   return ok();
 }
 

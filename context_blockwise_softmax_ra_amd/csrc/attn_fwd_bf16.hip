@@ -61,7 +61,9 @@ constexpr float kRescaleLog2 = 8.0f;
 
 // MODE: 0 = one non-causal block, 1 = one causal block (both as described by
 // the AttnArgs parts), 2 = a rank's whole share: the C blocks of RankKV in
-// ring order, merged in registers (no partials, no separate merge).
+// ring order, merged in registers (no partials, no separate merge), 3 = a
+// rectangle list (AttnArgs::segs): "segment" s is rectangle s, with its own
+// query rows, key range and diagonal offset (other shard maps).
 template <int DQK, int DV, int MODE, bool MERGE, bool OUT_BF16>
 __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV rk) {
   using G = Geo<DQK, DV>;
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
   const int group = a.group;
   // causal work only (one causal block, or a rank share of one block):
   // deal query tiles over the XCDs; otherwise contiguous ranges per XCD
-  const bool causal_only = MODE == 1 || (MODE == 2 && rk.cp == 1);
+  const bool causal_only = MODE == 1 || MODE == 3 || (MODE == 2 && rk.cp == 1);
   int b = causal_only ? xcd_deal(blockIdx.x, nb, group) : xcd_remap(blockIdx.x, nb);
   const int hg = b % group;
   b /= group;
@@ -88,8 +90,21 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
   const int qt = MODE != 0 ? (a.n_qtiles - 1 - qt_rev) : qt_rev;
   const int h = kvh * group + hg;
 
-  int q_lo, q_hi;
-  part_range(a.cu_q[seg], a.cu_q[seg + 1], MODE == 2 ? RA_PART_ALL : a.q_part, &q_lo, &q_hi);
+  int q_lo, q_hi, kseg0, kseg1, seg_diag = 0;
+  if (MODE == 3) {
+    const ra_segment sg = a.segs[seg];
+    q_lo = sg.q_lo;
+    q_hi = sg.q_hi;
+    kseg0 = sg.k_lo;
+    kseg1 = sg.k_hi;
+    seg_diag = sg.diag;
+  } else {
+    part_range(a.cu_q[seg], a.cu_q[seg + 1], MODE == 2 ? RA_PART_ALL : a.q_part, &q_lo, &q_hi);
+    // key segment bounds, read once: a vector load inside the tile loop
+    // would make the wave wait for its outstanding prefetch
+    kseg0 = a.cu_k[seg];
+    kseg1 = a.cu_k[seg + 1];
+  }
   const int q0 = q_lo + qt * BM;
   if (q0 >= q_hi) return;
   const int qhalf = (q_hi - q_lo) >> 1;  // second-half rows start here (part-relative)
@@ -109,9 +124,6 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
   const int my_row_rel = my_row - q_lo;
   const int64_t ks_bytes = a.k_stride * 2, vs_bytes = a.v_stride * 2;
   const int nblocks = MODE == 2 ? rk.cp : 1;
-  // key segment bounds, read once: a vector load inside the tile loop would
-  // make the wave wait for its outstanding prefetch
-  const int kseg0 = a.cu_k[seg], kseg1 = a.cu_k[seg + 1];
 
   // block bi of this workgroup, with the number of key tiles it visits
   auto get_block = [&](int bi) -> Block {
@@ -131,15 +143,20 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
       kp = a.k;
       vp = a.v;
       blk.kind = MODE == 1 ? KIND_CAUSAL : KIND_ALL;
-      kpart = a.k_part;
+      kpart = MODE == 3 ? RA_PART_ALL : a.k_part;
     }
     int k_lo, k_hi;
     part_range(kseg0, kseg1, kpart, &k_lo, &k_hi);
     blk.klen = k_hi - k_lo;
+    blk.diag = 0;
+    if (MODE == 3) {
+      blk.kind = seg_diag >= blk.klen ? KIND_ALL : KIND_CAUSAL;
+      blk.diag = seg_diag;
+    }
     blk.kb = reinterpret_cast<const char*>(kp) + ((int64_t)k_lo * a.k_stride + (int64_t)kvh * DQK) * 2;
     blk.vb = reinterpret_cast<const char*>(vp) + ((int64_t)k_lo * a.v_stride + (int64_t)kvh * DV) * 2;
     int kend = blk.klen;
-    if (blk.kind == KIND_CAUSAL) kend = min(blk.klen, qrel_last_wg + 1);
+    if (blk.kind == KIND_CAUSAL) kend = min(blk.klen, qrel_last_wg + blk.diag + 1);
     if (blk.kind == KIND_LATE_ROWS && qrel_last_wg < qhalf) kend = 0;
     blk.ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
     return blk;
@@ -222,12 +239,12 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
   auto tile = [&](const int gi, char* const stage, char* const next) __attribute__((always_inline)) {
     if (gi + 1 < total) issue_next(next);
     const int kt0 = cc.t * BN;  // relative to the block's first key
-    const int klen = cc.blk.klen, kind = cc.blk.kind;
+    const int klen = cc.blk.klen, kind = cc.blk.kind, diag = cc.blk.diag;
     // rows of this wave the tile can reach, and whether scores need a mask
     bool live = wave_live, need_mask;
     if (kind == KIND_CAUSAL) {
-      live = live && kt0 <= wq_last_rel;
-      need_mask = (kt0 + BN > klen) || (kt0 + BN - 1 > wq_first_rel);
+      live = live && kt0 <= wq_last_rel + diag;
+      need_mask = (kt0 + BN > klen) || (kt0 + BN - 1 > wq_first_rel + diag);
     } else if (kind == KIND_LATE_ROWS) {
       live = live && wq_last_rel >= qhalf;
       need_mask = (kt0 + BN > klen) || (wq_first_rel < qhalf);
@@ -257,7 +274,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int kr = kt0 + 32 * hh + ((i >> 3) << 4) + (g << 3) + (i & 7);
-            const bool ok = row_ok && (kr < klen) && (kind != KIND_CAUSAL || kr <= my_row_rel);
+            const bool ok = row_ok && (kr < klen) && (kind != KIND_CAUSAL || kr <= my_row_rel + diag);
             if (!ok) s[hh][i] = -INFINITY;
           }
       }
@@ -405,7 +422,29 @@ hipError_t launch_t(const AttnArgs& a, const RankKV* rk, bool causal, bool merge
   return hipGetLastError();
 }
 
+template <int DQK, int DV>
+hipError_t launch_seg_t(const AttnArgs& a, bool merge, hipStream_t st) {
+  const long long nblk = (long long)a.n_seq * a.hkv * a.n_qtiles * a.group;
+  if (nblk <= 0) return hipSuccess;
+  if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  dim3 grid((unsigned)nblk), block(NT);
+  RankKV none;
+  none.cp = 0;
+  none.rank = 0;
+  if (merge) hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, 3, true, false>), grid, block, 0, st, a, none);
+  else hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, 3, false, false>), grid, block, 0, st, a, none);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_attn_fwd_segments(const AttnArgs& a, int dqk, int dv, bool merge,
+                                    hipStream_t st) {
+  if (dqk == 128 && dv == 128) return launch_seg_t<128, 128>(a, merge, st);
+  if (dqk == 192 && dv == 128) return launch_seg_t<192, 128>(a, merge, st);
+  if (dqk == 64 && dv == 64) return launch_seg_t<64, 64>(a, merge, st);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int dqk, int dv, bool causal, bool merge,
                                 hipStream_t st) {

@@ -148,6 +148,7 @@ __global__ __launch_bounds__(PT, 1) void attn_fwd_pp_kernel(AttnArgs a, RankKV r
     int k_lo, k_hi;
     part_range(kseg0, kseg1, kpart, &k_lo, &k_hi);
     blk.klen = k_hi - k_lo;
+    blk.diag = 0;
     blk.kb = reinterpret_cast<const char*>(kp) + ((int64_t)k_lo * a.k_stride + (int64_t)kvh * DQK) * 2;
     blk.vb = reinterpret_cast<const char*>(vp) + ((int64_t)k_lo * a.v_stride + (int64_t)kvh * DV) * 2;
     int kend = blk.klen;

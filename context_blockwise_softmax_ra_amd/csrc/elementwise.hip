@@ -128,6 +128,24 @@ __global__ __launch_bounds__(NT) void zigzag_copy_kernel(const uint4* __restrict
   }
 }
 
+// Row copy by token index (other shard maps): gather dst[i] = src[tok[i]],
+// scatter dst[tok[i]] = src[i]; 16-byte words, grid-stride.
+__global__ __launch_bounds__(NT) void token_copy_kernel(const uint4* __restrict__ src,
+                                                        uint4* __restrict__ dst, int64_t row16,
+                                                        const int* __restrict__ tok, int n,
+                                                        int gather) {
+  const int64_t total = (int64_t)n * row16;
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < total; i += (int64_t)gridDim.x * NT) {
+    const int r = (int)(i / row16);
+    const int64_t w = i % row16;
+    const int64_t g = tok[r];
+    if (gather)
+      dst[(int64_t)r * row16 + w] = src[g * row16 + w];
+    else
+      dst[g * row16 + w] = src[(int64_t)r * row16 + w];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // delta[h, t] = sum_d dout[t, h, d] * out[t, h, d]
 // ---------------------------------------------------------------------------
@@ -203,6 +221,16 @@ hipError_t launch_zigzag_copy(const void* src, void* dst, int64_t row_bytes, int
   hipLaunchKernelGGL(zigzag_copy_kernel, grid, dim3(NT), 0, st,
                      reinterpret_cast<const uint4*>(src), reinterpret_cast<uint4*>(dst), row16,
                      cu_local, src_start, gather ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_tokens(const void* src, void* dst, int64_t row_bytes,
+                                const int32_t* tokens, int32_t n, bool gather, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int64_t row16 = row_bytes / 16;
+  hipLaunchKernelGGL(token_copy_kernel, dim3(grid_for((int64_t)n * row16, NT, 8192u)), dim3(NT), 0,
+                     st, reinterpret_cast<const uint4*>(src), reinterpret_cast<uint4*>(dst), row16,
+                     tokens, n, gather ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -134,7 +134,7 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 
 // How a KV block meets the rows of a workgroup.
 enum BlockKind {
-  KIND_CAUSAL = 0,     // key j visible to row i iff j <= i (part-relative)
+  KIND_CAUSAL = 0,     // key j visible to row i iff j <= i + diag (part-relative)
   KIND_ALL = 1,        // every key visible
   KIND_LATE_ROWS = 2,  // every key visible to rows of the segment's second half only
 };
@@ -144,6 +144,7 @@ struct Block {
   const char* vb;
   int klen;
   int kind;
+  int diag;        // KIND_CAUSAL: diagonal offset (0 except for rectangle lists)
   int ntiles;
 };
 

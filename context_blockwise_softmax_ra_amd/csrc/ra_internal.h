@@ -29,6 +29,7 @@ struct AttnArgs {
   int32_t n_seq;
   const int32_t* cu_q;
   const int32_t* cu_k;
+  const ra_segment* segs;  // rectangle list (segment-list launches), else NULL
   int32_t q_part, k_part;
   int32_t n_qtiles;       // query tiles per segment (max over segments)
   int32_t n_ktiles;       // key tiles per segment (max over segments; backward)
@@ -76,6 +77,10 @@ hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int dqk, int dv, bool causal,
                                 hipStream_t st);
 hipError_t launch_rank_fwd_bf16(const AttnArgs& a, const RankKV& rk, int dqk, int dv,
                                 bool out_bf16, hipStream_t st);
+hipError_t launch_attn_fwd_segments(const AttnArgs& a, int dqk, int dv, bool merge,
+                                    hipStream_t st);
+hipError_t launch_gather_tokens(const void* src, void* dst, int64_t row_bytes,
+                                const int32_t* tokens, int32_t n, bool gather, hipStream_t st);
 hipError_t launch_attn_fwd_pp(const AttnArgs& a, int dqk, int dv, bool causal, bool merge,
                               hipStream_t st);
 hipError_t launch_rank_fwd_pp(const AttnArgs& a, const RankKV& rk, int dqk, int dv,

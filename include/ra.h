@@ -270,6 +270,82 @@ ra_status ra_block_attn_work(const ra_attn_desc* d, int64_t* visible_pairs,
                              int64_t* tiles_visited, int64_t* tiles_skipped);
 
 /*
+ * Other shard maps, on the same kernels (the oh-bug page's correctness
+ * section on causal rank imbalance names contiguous ranges, striped /
+ * interleaved tokens and the zig-zag mapping; applying the zig-zag to a
+ * packed stream as a whole is the static split it warns about for varlen
+ * batches):
+ *   RA_MAP_ZIGZAG         per-document zig-zag (as ra_zigzag_shard_map)
+ *   RA_MAP_ZIGZAG_GLOBAL  zig-zag over the packed stream: its T tokens cut
+ *                         into 2C chunks regardless of documents, rank r
+ *                         holding chunks r and 2C-1-r (T % 2C == 0)
+ *   RA_MAP_STRIPED        token t on rank t mod C (T % C == 0)
+ *   RA_MAP_CONTIGUOUS     tokens [r T/C, (r+1) T/C) on rank r (T % C == 0)
+ * Every map gives each rank T/C tokens, kept in global order.
+ */
+typedef enum {
+  RA_MAP_ZIGZAG = 0,
+  RA_MAP_ZIGZAG_GLOBAL = 1,
+  RA_MAP_STRIPED = 2,
+  RA_MAP_CONTIGUOUS = 3
+} ra_map;
+
+/* Global token index of each local row of `rank` (host).  tokens: host
+ * int32[capacity], capacity >= T / cp_size; *n_tokens receives T / cp_size. */
+ra_status ra_shard_tokens(ra_map kind, int32_t cp_size, int32_t rank, int32_t n_seq,
+                          const int32_t* cu_seqlens_global, int32_t* tokens, int32_t capacity,
+                          int32_t* n_tokens);
+
+/* A rectangle of one ring step: local query rows [q_lo, q_hi) of the rank
+ * and local keys [k_lo, k_hi) of the KV block it holds; key j is visible to
+ * row i iff (j - k_lo) <= (i - q_lo) + diag (diag >= k_hi - k_lo: every key
+ * of the rectangle). */
+typedef struct ra_segment {
+  int32_t q_lo, q_hi, k_lo, k_hi, diag;
+} ra_segment;
+
+/* The rectangles of `rank`'s rows against the KV block of `owner` under a
+ * shard map: exactly the pairs of the global rule (same document, key not
+ * after query) between the two ranks' tokens, with disjoint row ranges, in
+ * row order (host).  segs: host array[capacity]; *n_segs receives the
+ * count (at most 2 x n_seq + 2); RA_ERR_INVALID_ARG if capacity is short. */
+ra_status ra_step_segments(ra_map kind, int32_t cp_size, int32_t rank, int32_t owner,
+                           int32_t n_seq, const int32_t* cu_seqlens_global, ra_segment* segs,
+                           int32_t capacity, int32_t* n_segs);
+
+/* Row gather / scatter by token index: gather writes dst row i = src row
+ * tokens[i], scatter writes dst row tokens[i] = src row i, for i < n.  Rows
+ * of row_bytes (a multiple of 16; buffers 16-byte aligned).  tokens_dev is
+ * the device copy of tokens_host; every index must be < n_rows (the row
+ * count of the indexed buffer: src for gather, dst for scatter). */
+ra_status ra_gather_tokens(const void* src, void* dst, int64_t row_bytes, int32_t n_rows,
+                           const int32_t* tokens_dev, const int32_t* tokens_host, int32_t n,
+                           void* stream);
+ra_status ra_scatter_tokens(const void* src, void* dst, int64_t row_bytes, int32_t n_rows,
+                            const int32_t* tokens_dev, const int32_t* tokens_host, int32_t n,
+                            void* stream);
+
+/* Block attention (bf16) over a list of rectangles, each with its own
+ * visibility rule, in one launch (the 4-wave kernel).  `d` supplies q, k,
+ * v, dtype, heads, dims and token strides; d->n_seq must be 1 with
+ * cu_seqlens_q_host = {0, Tq} and cu_seqlens_k_host = {0, Tk} (the buffer
+ * row counts; the device cu arrays and q_part / k_part / causal are not
+ * used).  segs_dev / segs_host: device array and host copy of n_seg
+ * rectangles within the buffers and with disjoint row ranges.  merge = 0
+ * writes the partial (out, lse) of every covered row (a row that sees no
+ * key gets (0, -inf)); merge = 1 folds it into (out, lse) as
+ * ra_block_attn_fwd_merge.  Rows outside every rectangle are untouched. */
+ra_status ra_block_attn_fwd_segments(const ra_attn_desc* d, int32_t n_seg,
+                                     const ra_segment* segs_dev, const ra_segment* segs_host,
+                                     float* out, float* lse, int32_t merge, void* stream);
+
+/* Accounting of a rectangle list for hq query heads: visible (query, key)
+ * pairs, key tiles the forward kernel visits and tiles it skips as entirely
+ * masked (host). */
+ra_status ra_segments_work(const ra_segment* segs, int32_t n_seg, int32_t hq,
+                           int64_t* visible_pairs, int64_t* tiles_visited, int64_t* tiles_skipped);
+
+/*
  * Name of the bf16 forward kernel a launch over the rows of q_part of `d`
  * uses (ra_block_attn_fwd / _merge with d->q_part, ra_rank_forward with
  * fuse_merge = 2 and RA_PART_ALL): "attn_fwd_pp" (8 waves, 256-row query

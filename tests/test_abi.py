@@ -270,3 +270,94 @@ def test_forward_kernel_choice_rejects_bad_input():
         L.ra_forward_kernel(d, 7)
     assert L.lib().ra_forward_kernel(None, 0) is None
     assert "NULL" in L.ra_last_error()
+
+
+# ---------------------------------------------------------------------------
+# other shard maps: token lists and step rectangles vs the oracle (host only)
+# ---------------------------------------------------------------------------
+
+MAP_CASES = [([64], 4), ([16, 48, 8, 56], 4), ([13, 51, 9, 55], 4), ([32, 96], 8),
+             ([40, 8, 24, 56, 8, 120], 2), ([7, 1, 24], 2)]
+
+
+def _expand(segs, nq, nk):
+    vis = np.zeros((nq, nk), bool)
+    for q_lo, q_hi, k_lo, k_hi, diag in segs:
+        for i in range(q_lo, q_hi):
+            for j in range(k_lo, k_hi):
+                if j - k_lo <= i - q_lo + diag:
+                    vis[i, j] = True
+    return vis
+
+
+def _map_ok(kind, lengths, C):
+    T = sum(lengths)
+    if kind == "zigzag":
+        return all(x % (2 * C) == 0 for x in lengths)
+    return T % (2 * C if kind == "zigzag_global" else C) == 0
+
+
+@pytest.mark.parametrize("kind", list(L.MAPS))
+@pytest.mark.parametrize("lengths,C", MAP_CASES)
+def test_shard_tokens_match_oracle(kind, lengths, C):
+    cu = synth.cu_seqlens(lengths)
+    if not _map_ok(kind, lengths, C):
+        with pytest.raises(L.RaError):
+            L.ra_shard_tokens(kind, C, 0, cu)
+        return
+    for r in range(C):
+        assert np.array_equal(L.ra_shard_tokens(kind, C, r, cu),
+                              oracle.map_local_tokens(kind, C, r, cu))
+
+
+@pytest.mark.parametrize("kind", list(L.MAPS))
+@pytest.mark.parametrize("lengths,C", MAP_CASES)
+def test_step_segments_are_exactly_the_visible_pairs(kind, lengths, C):
+    cu = synth.cu_seqlens(lengths)
+    if not _map_ok(kind, lengths, C):
+        return
+    T = sum(lengths)
+    for r in range(C):
+        for o in range(C):
+            segs = L.ra_step_segments(kind, C, r, o, cu)
+            ref = oracle.step_visible(kind, cu, C, r, o)
+            assert np.array_equal(_expand(segs, T // C, T // C), ref), (kind, r, o)
+            rows = sorted((int(a), int(b)) for a, b in segs[:, :2])
+            assert all(b0 <= a1 for (_, b0), (a1, _) in zip(rows, rows[1:]))   # disjoint rows
+            pairs, vis, skip = L.ra_segments_work(segs, 3)
+            assert pairs == 3 * int(ref.sum())
+            assert vis >= 0 and skip >= 0
+
+
+def test_segment_work_on_the_zigzag_matches_the_step_plan():
+    """The zig-zag rectangles cost the kernel the same pairs as the ring plan."""
+    cu = synth.cu_seqlens([64, 192, 32, 224])
+    C = 4
+    cu_local, _ = L.ra_zigzag_shard_map(C, 1, cu)
+    for s in range(C):
+        o = (1 - s) % C
+        segs = L.ra_step_segments("zigzag", C, 1, o, cu)
+        causal = s == 0
+        qp = 0 if (s == 0 or o < 1) else 2
+        kp = 1 if (s > 0 and o < 1) else 0
+        d = _desc(hq=2, hkv=2, cu=cu_local, q_part=qp, k_part=kp, causal=int(causal))
+        assert L.ra_segments_work(segs, 2)[0] == L.ra_block_attn_work(d)[0]
+
+
+def test_segment_launch_validation():
+    cu = np.array([0, 64], np.int32)
+    d = _desc(T=64, cu=cu)
+    segs = np.array([[0, 32, 0, 64, 0], [16, 48, 0, 64, 0]], np.int32)   # overlapping rows
+    st = L.lib().ra_block_attn_fwd_segments(ctypes.byref(d), 2, FAKE, segs.ctypes.data, FAKE,
+                                            FAKE, 0, None)
+    assert st == L.RA_ERR_INVALID_ARG and "overlap" in L.ra_last_error()
+    segs = np.array([[0, 65, 0, 64, 0]], np.int32)                       # beyond the rows
+    assert L.lib().ra_block_attn_fwd_segments(ctypes.byref(d), 1, FAKE, segs.ctypes.data, FAKE,
+                                              FAKE, 0, None) == L.RA_ERR_INVALID_ARG
+    d32 = _desc(T=64, cu=cu, dtype=L.RA_FP32, dqk=64, dv=64)
+    segs = np.array([[0, 8, 0, 8, 0]], np.int32)
+    assert L.lib().ra_block_attn_fwd_segments(ctypes.byref(d32), 1, FAKE, segs.ctypes.data, FAKE,
+                                              FAKE, 0, None) == L.RA_ERR_UNSUPPORTED
+    tok = np.array([0, 5], np.int32)
+    assert L.lib().ra_gather_tokens(FAKE, FAKE, 256, 5, FAKE, tok.ctypes.data, 2,
+                                    None) == L.RA_ERR_INVALID_ARG          # token 5 >= 5 rows

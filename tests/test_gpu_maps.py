@@ -1,0 +1,130 @@
+"""GPU parity of the other shard maps (striped, contiguous, stream-level
+zig-zag, and the zig-zag itself through the same path) against the oracle.
+
+A rank's share under a map is a sequence of rectangle launches
+(ra_block_attn_fwd_segments, one per ring step) merged into a running
+result; every rank's rows must equal the oracle's full attention rows.
+The rectangle launch itself is checked on random rectangles with negative,
+zero, positive and "every key" diagonal offsets, in both write and merge
+modes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import check_lse, check_out, global_inputs, log, to_np
+
+pytestmark = pytest.mark.gpu
+
+R = pytest.importorskip("context_blockwise_softmax_ra_amd")
+from context_blockwise_softmax_ra_amd import _lib as L  # noqa: E402
+from context_blockwise_softmax_ra_amd.maps import MapProblem  # noqa: E402
+
+DEV = torch.device("cuda:0")
+
+
+def _rect_ref(q, k, v, segs):
+    """Oracle partial of a rectangle list: for rectangle (q_lo, q_hi, k_lo,
+    k_hi, diag) key j is visible to row i iff j - k_lo <= i - q_lo + diag."""
+    Tq, hq, _ = q.shape
+    out = np.zeros((Tq, hq, v.shape[2]))
+    lse = np.full((hq, Tq), np.nan)
+    cov = np.zeros(Tq, bool)
+    for q_lo, q_hi, k_lo, k_hi, diag in segs:
+        if q_hi <= q_lo:
+            continue
+        qp = np.arange(q_hi - q_lo) + diag
+        kp = np.arange(k_hi - k_lo)
+        o, l = oracle.attention(q[q_lo:q_hi], k[k_lo:k_hi], v[k_lo:k_hi], qp, np.zeros_like(qp),
+                                kp, np.zeros_like(kp), causal=True)
+        out[q_lo:q_hi], lse[:, q_lo:q_hi], cov[q_lo:q_hi] = o, l, True
+    return out, lse, cov
+
+
+@pytest.mark.parametrize("dims", [(128, 128), (192, 128), (64, 64)])
+def test_rectangle_launch_edge_cases(dims):
+    dqk, dv = dims
+    Tq, Tk, hq, hkv = 700, 600, 4, 2
+    g = torch.Generator().manual_seed(dqk * 7 + dv)
+    q = torch.randn(Tq, hq, dqk, generator=g).to(torch.bfloat16)
+    k = torch.randn(Tk, hkv, dqk, generator=g).to(torch.bfloat16)
+    v = torch.randn(Tk, hkv, dv, generator=g).to(torch.bfloat16)
+    segs = np.array([
+        [0, 130, 0, 200, 0],        # causal, ragged
+        [130, 131, 5, 6, -1],       # one row that sees nothing
+        [131, 300, 100, 400, -1],   # strictly-below diagonal (striped, later owner)
+        [300, 420, 0, 64, 64],      # every key
+        [420, 421, 0, 0, 0],        # no keys
+        [421, 650, 200, 600, 150],  # diagonal far right: a full part then causal
+        [650, 700, 590, 600, -45],  # only the last rows see keys
+    ], np.int32)
+    desc = L.attn_desc(q.to(DEV), k.to(DEV), v.to(DEV), torch.zeros(2, dtype=torch.int32, device=DEV),
+                       torch.zeros(2, dtype=torch.int32, device=DEV), [0, Tq], [0, Tk])
+    sd = torch.from_numpy(segs).to(DEV)
+    ro, rl, cov = _rect_ref(to_np(q), to_np(k), to_np(v), segs)
+    out = torch.full((Tq, hq, dv), 7.0, device=DEV)
+    lse = torch.full((hq, Tq), 7.0, device=DEV)
+    L.ra_block_attn_fwd_segments(desc, sd, segs, out, lse)
+    torch.cuda.synchronize()
+    go, gl = to_np(out), to_np(lse)
+    check_out(go[cov], ro[cov], "bf16", f"rect {dims}")
+    check_lse(gl[:, cov], rl[:, cov], f"rect {dims}")
+    assert (go[~cov] == 7.0).all()
+    # merge into a random running result
+    acc_o = torch.randn((Tq, hq, dv), generator=g)
+    acc_l = torch.randn((hq, Tq), generator=g)
+    mo, ml = acc_o.clone().to(DEV), acc_l.clone().to(DEV)
+    L.ra_block_attn_fwd_segments(desc, sd, segs, mo, ml, merge=True)
+    torch.cuda.synchronize()
+    eo, el = oracle.lse_merge(to_np(acc_o), to_np(acc_l), ro, np.where(cov[None, :], rl, -np.inf))
+    check_out(to_np(mo)[cov], eo[cov], "bf16", f"rect merge {dims}")
+    check_lse(to_np(ml)[:, cov], el[:, cov], f"rect merge {dims}")
+
+
+def _map_parity(kind, w, ranks=None):
+    log(f"map {kind}: {w.name} S={w.seqlen} C={w.cp} hq={w.hq} hkv={w.hkv}")
+    q, k, v, _ = global_inputs(w)
+    prob = MapProblem(kind, q.to(DEV), k.to(DEV), v.to(DEV), w.cu_global(), w.cp)
+    q64, k64, v64 = to_np(q), to_np(k), to_np(v)
+    cu = w.cu_global()
+    for r in (range(w.cp) if ranks is None else ranks):
+        out, lse, acc = prob.alloc_forward()
+        prob.forward(r, out, lse, acc)
+        torch.cuda.synchronize()
+        ro, rl = oracle.full_attention(q64, k64, v64, cu, rows=prob.rows(r))
+        check_out(to_np(out), ro, w.dtype, f"{kind} rank{r}")
+        check_lse(to_np(lse), rl, f"{kind} rank{r}")
+    return prob
+
+
+@pytest.mark.parametrize("kind", list(L.MAPS))
+def test_map_shares_reduced_gqa(kind):
+    _map_parity(kind, synth.reduced("gqa_32k", 4096, 8))
+
+
+@pytest.mark.parametrize("kind", list(L.MAPS))
+def test_map_shares_reduced_varlen(kind):
+    w = synth.reduced("varlen_128k", 16384, 4)
+    w.doc_lengths = synth.doc_lengths_loguniform(4, 16384, 8, 4096, 8)
+    _map_parity(kind, w)
+
+
+def test_map_shares_full_size_sampled():
+    w = synth.WORKLOADS["gqa_32k"]
+    q, k, v, _ = global_inputs(w)
+    q64, k64, v64 = to_np(q), to_np(k), to_np(v)
+    cu = w.cu_global()
+    rng = np.random.default_rng(5)
+    for kind in ("striped", "zigzag_global"):
+        prob = MapProblem(kind, q.to(DEV), k.to(DEV), v.to(DEV), cu, w.cp)
+        for r in (0, 7):
+            out, lse, acc = prob.alloc_forward()
+            prob.forward(r, out, lse, acc)
+            torch.cuda.synchronize()
+            loc = np.sort(rng.choice(prob.Tl, 24, replace=False))
+            ro, rl = oracle.full_attention(q64, k64, v64, cu, rows=prob.rows(r)[loc])
+            check_out(to_np(out[torch.from_numpy(loc).to(DEV)]), ro, w.dtype, f"{kind} rank{r}")
+            check_lse(to_np(lse)[:, loc], rl, f"{kind} rank{r}")
+        del prob
