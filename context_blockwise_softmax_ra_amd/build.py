@@ -37,14 +37,14 @@ def sources():
 # Per-file flags.  The attention kernels take row maxima of matrix-core
 # outputs; without this, IEEE-mode fmaxf canonicalises every operand first
 # (one extra v_max_f32 per score).  NaN inputs still propagate to NaN outputs.
-# The backward kernels run one wave per SIMD with large accumulators; the
-# default MFMA register heuristic there shuttles values between the AGPR and
-# VGPR halves of the register file every iteration, so keep MFMA operands and
-# results in VGPRs.
+# The backward kernels run one wave per SIMD with large accumulators, which
+# live in the AGPR half of the register file (the compiler's default MFMA
+# form): with the tiles loaded straight into LDS that measured faster than
+# forcing MFMA results into VGPRs.
 PER_FILE = {
     "attn_fwd_bf16.hip": ["-fno-honor-nans"],
     "attn_fwd_pp.hip": ["-fno-honor-nans"],
-    "attn_bwd_bf16.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "attn_bwd_bf16.hip": ["-fno-honor-nans"],
 }
 
 

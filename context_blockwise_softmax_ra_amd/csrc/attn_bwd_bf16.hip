@@ -28,7 +28,13 @@
 //     dQ^T += K^T dS^T               A = K via transposing LDS reads.
 // Q, dO and K tiles are read both by 128-bit row reads and by transposing
 // reads, so they use the XOR-swizzled "dual" LDS layout (conflict-free for
-// both, see mfma_common.h).
+// both, see mfma_common.h).  Every tile goes from global memory straight
+// into LDS (buffer_load ... lds, DualLoader), double-buffered in separate LDS
+// objects: tile t+1 streams in while tile t is computed, and no registers
+// stage the prefetch.  The lse and delta of a query tile come along (4 bytes
+// per lane).  Each kernel runs one wave per SIMD (large accumulators), so
+// the LDS operand reads of a block of products are scheduled a few products
+// ahead (pipeline_lds_mfma).
 
 #include "mfma_common.h"
 
@@ -39,6 +45,12 @@ using namespace mfma;
 
 constexpr int NT = 256;
 constexpr float kLog2e = 1.4426950408889634f;
+// matrix-core products the LDS operand reads run ahead of (one wave per
+// SIMD here, so nothing else hides the read latency)
+#ifndef RA_BWD_AHEAD
+#define RA_BWD_AHEAD 4
+#endif
+constexpr int kBwdAhead = RA_BWD_AHEAD;
 
 __device__ __forceinline__ float lse_log2(const float* lse, int64_t i, bool valid) {
   // rows outside the part (or that see nothing) contribute P = 0
@@ -59,74 +71,21 @@ struct GeoKV {
   static constexpr int OROWB = 256;
   static constexpr int Q_BYTES = KV_BQ * QROWB;
   static constexpr int O_BYTES = KV_BQ * OROWB;
-  static constexpr int STAGE = Q_BYTES + O_BYTES + 2 * KV_BQ * 4;
-  static constexpr int QCH = DQK / 8, OCH = DV / 8;
-  static constexpr int Q_LD = KV_BQ * QCH / NT;
-  static constexpr int O_LD = KV_BQ * OCH / NT;
   static constexpr int KK = DQK / 16, VK = DV / 16;
   static constexpr int NQT = DQK / 32, NVT = DV / 32;
-  static_assert(KV_BQ * QCH % NT == 0 && KV_BQ * OCH % NT == 0, "tile split");
   static_assert(DV == 128, "dO rows are 256 bytes");
 };
-
-template <int DQK, int DV>
-struct PfKV {
-  u32x4 q[GeoKV<DQK, DV>::Q_LD];
-  u32x4 o[GeoKV<DQK, DV>::O_LD];
-  float ld;  // lse*log2e (threads 0..31) or delta (threads 32..63)
-};
-
-template <int DQK, int DV>
-__device__ __forceinline__ void kv_load(PfKV<DQK, DV>& pf, const AttnArgs& a, int h, int q0,
-                                        int q_hi, int tid) {
-  using G = GeoKV<DQK, DV>;
-  const __bf16* qb = reinterpret_cast<const __bf16*>(a.q) + (int64_t)h * DQK;
-  const __bf16* ob = reinterpret_cast<const __bf16*>(a.dout) + (int64_t)h * DV;
-#pragma unroll
-  for (int i = 0; i < G::Q_LD; ++i) {
-    const int idx = tid + NT * i;
-    const int row = idx / G::QCH, c = idx % G::QCH;
-    const int tok = min(q0 + row, q_hi - 1);
-    pf.q[i] = ldg16(qb + (int64_t)tok * a.q_stride + c * 8);
-  }
-#pragma unroll
-  for (int i = 0; i < G::O_LD; ++i) {
-    const int idx = tid + NT * i;
-    const int row = idx / G::OCH, c = idx % G::OCH;
-    const int tok = min(q0 + row, q_hi - 1);
-    pf.o[i] = ldg16(ob + (int64_t)tok * ((int64_t)a.hq * DV) + c * 8);
-  }
-  if (tid < 2 * KV_BQ) {
-    const int row = tid & (KV_BQ - 1);
-    const int tok = q0 + row;
-    const bool valid = tok < q_hi;
-    const int64_t i = (int64_t)h * a.total_q + (valid ? tok : 0);
-    pf.ld = tid < KV_BQ ? lse_log2(a.lse_in, i, valid) : (valid ? a.delta[i] : 0.f);
-  }
-}
-
-template <int DQK, int DV>
-__device__ __forceinline__ void kv_store(const PfKV<DQK, DV>& pf, char* st, int tid) {
-  using G = GeoKV<DQK, DV>;
-#pragma unroll
-  for (int i = 0; i < G::Q_LD; ++i) {
-    const int idx = tid + NT * i;
-    const int row = idx / G::QCH, c = idx % G::QCH;
-    *reinterpret_cast<u32x4*>(st + dual_off<G::QROWB>(row, c * 16)) = pf.q[i];
-  }
-#pragma unroll
-  for (int i = 0; i < G::O_LD; ++i) {
-    const int idx = tid + NT * i;
-    const int row = idx / G::OCH, c = idx % G::OCH;
-    *reinterpret_cast<u32x4*>(st + G::Q_BYTES + dual_off<G::OROWB>(row, c * 16)) = pf.o[i];
-  }
-  if (tid < 2 * KV_BQ) reinterpret_cast<float*>(st + G::Q_BYTES + G::O_BYTES)[tid] = pf.ld;
-}
 
 template <int DQK, int DV, bool CAUSAL>
 __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
   using G = GeoKV<DQK, DV>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE];
+  // per stage: Q tile, dO tile, lse (rows 0..31) and delta (32..63)
+  __shared__ __attribute__((aligned(1024))) char qs0[G::Q_BYTES];
+  __shared__ __attribute__((aligned(1024))) char qs1[G::Q_BYTES];
+  __shared__ __attribute__((aligned(1024))) char os0[G::O_BYTES];
+  __shared__ __attribute__((aligned(1024))) char os1[G::O_BYTES];
+  __shared__ __attribute__((aligned(256))) float ld0[2 * KV_BQ];
+  __shared__ __attribute__((aligned(256))) float ld1[2 * KV_BQ];
 
   int b = xcd_remap(blockIdx.x, gridDim.x);
   const int kt = b % a.n_ktiles;
@@ -141,7 +100,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
   const int qlen = q_hi - q_lo, klen = k_hi - k_lo;
   if (k0 >= k_hi || qlen <= 0) return;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
   const int wk_rel = kt * KV_BN + wave * 32;        // first key of the wave (part-relative)
   const bool wave_live = wk_rel < klen;
@@ -174,76 +133,102 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
   const int arow = sigma(l32);  // A-operand row of this lane (query row in the tile)
   const int trr = tr_row(lane), trc = tr_col_bytes(lane);
 
-  PfKV<DQK, DV> pf;
   auto it_head = [&](int it) { return kvh * a.group + it / per_head; };
   auto it_q0 = [&](int it) { return q_lo + (qt_begin + it % per_head) * KV_BQ; };
-  if (n_it > 0) {
-    kv_load<DQK, DV>(pf, a, it_head(0), it_q0(0), q_hi, tid);
-    kv_store<DQK, DV>(pf, smem, tid);
-    if (n_it > 1) kv_load<DQK, DV>(pf, a, it_head(1), it_q0(1), q_hi, tid);
-  }
-  __syncthreads();
+  DualLoader<KV_BQ, DQK, G::QROWB, NT / 64> lq;
+  DualLoader<KV_BQ, DV, G::OROWB, NT / 64> lo;
+  const int64_t qsb = a.q_stride * 2, osb = (int64_t)a.hq * DV * 2;
+  lq.init(qsb, wave, lane);
+  lo.init(osb, wave, lane);
+  // tile it's Q, dO, lse and delta into one stage (rows past the part are
+  // clamped to its last row here and masked in the products)
+  auto issue = [&](int it, char* qd, char* od, float* ldd) __attribute__((always_inline)) {
+    const int h = it_head(it), q0 = it_q0(it), rows_left = q_hi - q0;
+    lq.issue(reinterpret_cast<const char*>(a.q) + ((int64_t)q0 * a.q_stride + (int64_t)h * DQK) * 2,
+             qsb, rows_left, qd);
+    lo.issue(reinterpret_cast<const char*>(a.dout) + ((int64_t)q0 * a.hq + h) * DV * 2, osb,
+             rows_left, od);
+    if (wave == 0) {
+      const uint32_t r4 = (uint32_t)min(lane & (KV_BQ - 1), rows_left - 1) * 4;
+      const int64_t i0 = (int64_t)h * a.total_q + q0;
+      if (lane < KV_BQ) g2lds4(tile_rsrc(a.lse_in + i0), r4, ldd);
+      else g2lds4(tile_rsrc(a.delta + i0), r4, ldd);
+    }
+  };
 
-  for (int it = 0; it < n_it; ++it) {
-    const char* st = smem + (it & 1) * G::STAGE;
+  // products of tile it from one stage
+  auto tile = [&](int it, const char* qs, const char* os, const float* lsd)
+      __attribute__((always_inline)) {
     const int qt_rel = (qt_begin + it % per_head) * KV_BQ;  // first query row (part-relative)
     const bool live = wave_live && (!CAUSAL || qt_rel + KV_BQ - 1 >= wk_rel);
-    if (live) {
-      const char* qs = st;
-      const char* os = st + G::Q_BYTES;
-      const float* lsd = reinterpret_cast<const float*>(st + G::Q_BYTES + G::O_BYTES);
-      // S = Q K^T and dP = dO V^T, lane = key column, entry i = query row
-      // 16*(i/8) + 8g + i%8 of the tile
-      f32x16 s = zero16(), dp = zero16();
+    if (!live) return;
+    // S = Q K^T and dP = dO V^T, lane = key column, entry i = query row
+    // 16*(i/8) + 8g + i%8 of the tile
+    f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-      for (int kk = 0; kk < G::KK; ++kk)
-        s = mma(as_bf16x8(lds16(qs + dual_off<G::QROWB>(arow, (16 * kk + 8 * g) * 2))), kf[kk], s);
+    for (int kk = 0; kk < G::KK; ++kk)
+      s = mma(as_bf16x8(lds16(qs + dual_off<G::QROWB>(arow, (16 * kk + 8 * g) * 2))), kf[kk], s);
 #pragma unroll
-      for (int kk = 0; kk < G::VK; ++kk)
-        dp = mma(as_bf16x8(lds16(os + dual_off<G::OROWB>(arow, (16 * kk + 8 * g) * 2))), vf[kk],
-                 dp);
-      const bool need_mask =
-          (my_key_rel >= klen) || (wk_rel + 31 >= klen) || (CAUSAL && qt_rel < wk_rel + 31);
+    for (int kk = 0; kk < G::VK; ++kk)
+      dp = mma(as_bf16x8(lds16(os + dual_off<G::OROWB>(arow, (16 * kk + 8 * g) * 2))), vf[kk], dp);
+    pipeline_lds_mfma<G::KK + G::VK, 1, kBwdAhead>();
+    __builtin_amdgcn_sched_barrier(0);
+    const bool need_mask = (my_key_rel >= klen) || (wk_rel + 31 >= klen) ||
+                           (CAUSAL && qt_rel < wk_rel + 31) || (qt_rel + KV_BQ > qlen);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = 16 * (i >> 3) + 8 * g + (i & 7);
-        const float l2 = lsd[r];
-        const float dl = lsd[KV_BQ + r];
-        float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -l2));
-        if (need_mask) {
-          const bool ok = (my_key_rel < klen) && (!CAUSAL || my_key_rel <= qt_rel + r);
-          p = ok ? p : 0.f;
-        }
-        s[i] = p;
-        dp[i] = p * (dp[i] - dl);
+    for (int i = 0; i < 16; ++i) {
+      const int r = 16 * (i >> 3) + 8 * g + (i & 7);
+      const float lr = lsd[r];
+      const float l2 = lr == -INFINITY ? INFINITY : lr * kLog2e;  // rows that see nothing: P = 0
+      const float dl = lsd[KV_BQ + r];
+      float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -l2));
+      if (need_mask) {
+        const bool ok = (my_key_rel < klen) && (qt_rel + r < qlen) &&
+                        (!CAUSAL || my_key_rel <= qt_rel + r);
+        p = ok ? p : 0.f;
       }
-      const bf16x8 pp0 = pack8(s, 0), pp1 = pack8(s, 8);
-      const bf16x8 ds0 = pack8(dp, 0), ds1 = pack8(dp, 8);
-      // dV += P^T dO,  dK += dS^T Q   (B via transposing reads)
+      s[i] = p;
+      dp[i] = p * (dp[i] - dl);
+    }
+    const bf16x8 pp0 = pack8(s, 0), pp1 = pack8(s, 8);
+    const bf16x8 ds0 = pack8(dp, 0), ds1 = pack8(dp, 8);
+    __builtin_amdgcn_sched_barrier(0);
+    // dV += P^T dO,  dK += dS^T Q   (B via transposing reads)
 #pragma unroll
-      for (int bb = 0; bb < 2; ++bb) {
-        const int row = 16 * bb + trr;
+    for (int bb = 0; bb < 2; ++bb) {
+      const int row = 16 * bb + trr;
 #pragma unroll
-        for (int nt = 0; nt < G::NVT; ++nt) {
-          const int col = 64 * nt + trc;
-          const bf16x8 bo = cat_tr(lds_tr(os + dual_off<G::OROWB>(row, col)),
-                                   lds_tr(os + dual_off<G::OROWB>(row + 4, col)));
-          dv[nt] = mma(bb ? pp1 : pp0, bo, dv[nt]);
-        }
+      for (int nt = 0; nt < G::NVT; ++nt) {
+        const int col = 64 * nt + trc;
+        const bf16x8 bo = cat_tr(lds_tr(os + dual_off<G::OROWB>(row, col)),
+                                 lds_tr(os + dual_off<G::OROWB>(row + 4, col)));
+        dv[nt] = mma(bb ? pp1 : pp0, bo, dv[nt]);
+      }
 #pragma unroll
-        for (int nt = 0; nt < G::NQT; ++nt) {
-          const int col = 64 * nt + trc;
-          const bf16x8 bq = cat_tr(lds_tr(qs + dual_off<G::QROWB>(row, col)),
-                                   lds_tr(qs + dual_off<G::QROWB>(row + 4, col)));
-          dk[nt] = mma(bb ? ds1 : ds0, bq, dk[nt]);
-        }
+      for (int nt = 0; nt < G::NQT; ++nt) {
+        const int col = 64 * nt + trc;
+        const bf16x8 bq = cat_tr(lds_tr(qs + dual_off<G::QROWB>(row, col)),
+                                 lds_tr(qs + dual_off<G::QROWB>(row + 4, col)));
+        dk[nt] = mma(bb ? ds1 : ds0, bq, dk[nt]);
       }
     }
-    if (it + 1 < n_it) {
-      kv_store<DQK, DV>(pf, smem + ((it + 1) & 1) * G::STAGE, tid);
-      __syncthreads();
-      if (it + 2 < n_it) kv_load<DQK, DV>(pf, a, it_head(it + 2), it_q0(it + 2), q_hi, tid);
-    }
+    pipeline_lds_mfma<2 * (G::NVT + G::NQT), 2, kBwdAhead>();
+  };
+
+  if (n_it > 0) issue(0, qs0, os0, ld0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  auto step = [&](int it, const char* qs, const char* os, const float* lsd, char* qn, char* on,
+                  float* ln) __attribute__((always_inline)) {
+    if (it + 1 < n_it) issue(it + 1, qn, on, ln);
+    tile(it, qs, os, lsd);
+    // next tile landed (own loads) and every wave is done with this one
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  for (int it = 0; it < n_it; it += 2) {
+    step(it, qs0, os0, ld0, qs1, os1, ld1);
+    if (it + 1 < n_it) step(it + 1, qs1, os1, ld1, qs0, os0, ld0);
   }
   if (!wave_live) return;
 
@@ -275,60 +260,18 @@ struct GeoQ {
   static constexpr int VROWB = 256;
   static constexpr int K_BYTES = Q_BN * KROWB;
   static constexpr int V_BYTES = Q_BN * VROWB;
-  static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int KCH = DQK / 8, VCH = DV / 8;
-  static constexpr int K_LD = Q_BN * KCH / NT;
-  static constexpr int V_LD = Q_BN * VCH / NT;
   static constexpr int KK = DQK / 16, VK = DV / 16;
   static constexpr int NQT = DQK / 32;
   static_assert(DV == 128, "V rows are 256 bytes");
 };
 
-template <int DQK, int DV>
-struct PfQ {
-  u32x4 k[GeoQ<DQK, DV>::K_LD];
-  u32x4 v[GeoQ<DQK, DV>::V_LD];
-};
-
-template <int DQK, int DV>
-__device__ __forceinline__ void q_load(PfQ<DQK, DV>& pf, const __bf16* kb, const __bf16* vb,
-                                       int64_t ks, int64_t vs, int key0, int k_last, int tid) {
-  using G = GeoQ<DQK, DV>;
-#pragma unroll
-  for (int i = 0; i < G::K_LD; ++i) {
-    const int idx = tid + NT * i;
-    const int row = idx / G::KCH, c = idx % G::KCH;
-    pf.k[i] = ldg16(kb + (int64_t)min(key0 + row, k_last) * ks + c * 8);
-  }
-#pragma unroll
-  for (int i = 0; i < G::V_LD; ++i) {
-    const int idx = tid + NT * i;
-    const int row = idx / G::VCH, c = idx % G::VCH;
-    pf.v[i] = ldg16(vb + (int64_t)min(key0 + row, k_last) * vs + c * 8);
-  }
-}
-
-template <int DQK, int DV>
-__device__ __forceinline__ void q_store(const PfQ<DQK, DV>& pf, char* st, int tid) {
-  using G = GeoQ<DQK, DV>;
-#pragma unroll
-  for (int i = 0; i < G::K_LD; ++i) {
-    const int idx = tid + NT * i;
-    const int row = idx / G::KCH, c = idx % G::KCH;
-    *reinterpret_cast<u32x4*>(st + dual_off<G::KROWB>(row, c * 16)) = pf.k[i];
-  }
-#pragma unroll
-  for (int i = 0; i < G::V_LD; ++i) {
-    const int idx = tid + NT * i;
-    const int row = idx / G::VCH, c = idx % G::VCH;
-    *reinterpret_cast<u32x4*>(st + G::K_BYTES + dual_off<G::VROWB>(row, c * 16)) = pf.v[i];
-  }
-}
-
 template <int DQK, int DV, bool CAUSAL>
 __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a) {
   using G = GeoQ<DQK, DV>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE];
+  __shared__ __attribute__((aligned(1024))) char ks0[G::K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char ks1[G::K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vs0[G::V_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vs1[G::V_BYTES];
 
   int b = xcd_remap(blockIdx.x, gridDim.x);
   const int hg = b % a.group;
@@ -348,7 +291,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a) {
   const int klen = k_hi - k_lo;
   if (klen <= 0) return;  // nothing to add
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
   const int wq0 = q0 + wave * 32;
   const bool wave_live = wq0 < q_hi;
@@ -383,71 +326,80 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a) {
 #pragma unroll
   for (int t = 0; t < G::NQT; ++t) dq[t] = zero16();
 
-  const __bf16* kb = reinterpret_cast<const __bf16*>(a.k) + (int64_t)kvh * DQK;
-  const __bf16* vb = reinterpret_cast<const __bf16*>(a.v) + (int64_t)kvh * DV;
-  const int k_last = k_hi - 1;
+  const char* kb = reinterpret_cast<const char*>(a.k) + ((int64_t)k_lo * a.k_stride + (int64_t)kvh * DQK) * 2;
+  const char* vb = reinterpret_cast<const char*>(a.v) + ((int64_t)k_lo * a.v_stride + (int64_t)kvh * DV) * 2;
+  const int64_t ksb = a.k_stride * 2, vsb = a.v_stride * 2;
   const int arow = sigma(l32);
   const int trr = tr_row(lane), trc = tr_col_bytes(lane);
+  DualLoader<Q_BN, DQK, G::KROWB, NT / 64> lk;
+  DualLoader<Q_BN, DV, G::VROWB, NT / 64> lv;
+  lk.init(ksb, wave, lane);
+  lv.init(vsb, wave, lane);
+  auto issue = [&](int t, char* kd, char* vd) __attribute__((always_inline)) {
+    const int rows_left = klen - t * Q_BN;
+    lk.issue(kb + (int64_t)t * Q_BN * ksb, ksb, rows_left, kd);
+    lv.issue(vb + (int64_t)t * Q_BN * vsb, vsb, rows_left, vd);
+  };
 
-  PfQ<DQK, DV> pf;
-  if (ntiles > 0) {
-    q_load<DQK, DV>(pf, kb, vb, a.k_stride, a.v_stride, k_lo, k_last, tid);
-    q_store<DQK, DV>(pf, smem, tid);
-    if (ntiles > 1) q_load<DQK, DV>(pf, kb, vb, a.k_stride, a.v_stride, k_lo + Q_BN, k_last, tid);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const char* st = smem + (t & 1) * G::STAGE;
+  auto tile = [&](int t, const char* ks, const char* vs) __attribute__((always_inline)) {
     const int kt0 = t * Q_BN;
-    if (wave_live && kt0 < wave_kend) {
-      const char* ks = st;
-      const char* vs = st + G::K_BYTES;
-      const bool need_mask = (kt0 + Q_BN > wave_kend) || (CAUSAL && kt0 + Q_BN - 1 > wq_first_rel);
-      bf16x8 dsp[4];
+    if (!(wave_live && kt0 < wave_kend)) return;
+    const bool need_mask = (kt0 + Q_BN > wave_kend) || (CAUSAL && kt0 + Q_BN - 1 > wq_first_rel);
+    bf16x8 dsp[4];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        f32x16 s = zero16(), dp = zero16();
-        const int kr = arow + 32 * hh;
+    for (int hh = 0; hh < 2; ++hh) {
+      f32x16 s = zero16(), dp = zero16();
+      const int kr = arow + 32 * hh;
 #pragma unroll
-        for (int kk = 0; kk < G::KK; ++kk)
-          s = mma(as_bf16x8(lds16(ks + dual_off<G::KROWB>(kr, (16 * kk + 8 * g) * 2))), qf[kk], s);
+      for (int kk = 0; kk < G::KK; ++kk)
+        s = mma(as_bf16x8(lds16(ks + dual_off<G::KROWB>(kr, (16 * kk + 8 * g) * 2))), qf[kk], s);
 #pragma unroll
-        for (int kk = 0; kk < G::VK; ++kk)
-          dp = mma(as_bf16x8(lds16(vs + dual_off<G::VROWB>(kr, (16 * kk + 8 * g) * 2))), of[kk],
-                   dp);
+      for (int kk = 0; kk < G::VK; ++kk)
+        dp = mma(as_bf16x8(lds16(vs + dual_off<G::VROWB>(kr, (16 * kk + 8 * g) * 2))), of[kk], dp);
+      pipeline_lds_mfma<G::KK + G::VK, 1, kBwdAhead>();
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -l2));
-          if (need_mask) {
-            const int key = kt0 + 32 * hh + 16 * (i >> 3) + 8 * g + (i & 7);
-            const bool ok = key < klen && (!CAUSAL || key <= my_row_rel);
-            p = ok ? p : 0.f;
-          }
-          dp[i] = p * (dp[i] - dl);
+      for (int i = 0; i < 16; ++i) {
+        float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -l2));
+        if (need_mask) {
+          const int key = kt0 + 32 * hh + 16 * (i >> 3) + 8 * g + (i & 7);
+          const bool ok = key < klen && (!CAUSAL || key <= my_row_rel);
+          p = ok ? p : 0.f;
         }
-        dsp[2 * hh] = pack8(dp, 0);
-        dsp[2 * hh + 1] = pack8(dp, 8);
+        dp[i] = p * (dp[i] - dl);
       }
-      // dQ^T += K^T dS^T, A = K^T by transposing reads of the K tile
+      dsp[2 * hh] = pack8(dp, 0);
+      dsp[2 * hh + 1] = pack8(dp, 8);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // dQ^T += K^T dS^T, A = K^T by transposing reads of the K tile
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const int r = 16 * bb + trr;
+    for (int bb = 0; bb < 4; ++bb) {
+      const int r = 16 * bb + trr;
 #pragma unroll
-        for (int nt = 0; nt < G::NQT; ++nt) {
-          const int col = 64 * nt + trc;
-          const bf16x8 ka = cat_tr(lds_tr(ks + dual_off<G::KROWB>(r, col)),
-                                   lds_tr(ks + dual_off<G::KROWB>(r + 4, col)));
-          dq[nt] = mma(ka, dsp[bb], dq[nt]);
-        }
+      for (int nt = 0; nt < G::NQT; ++nt) {
+        const int col = 64 * nt + trc;
+        const bf16x8 ka = cat_tr(lds_tr(ks + dual_off<G::KROWB>(r, col)),
+                                 lds_tr(ks + dual_off<G::KROWB>(r + 4, col)));
+        dq[nt] = mma(ka, dsp[bb], dq[nt]);
       }
     }
-    if (t + 1 < ntiles) {
-      q_store<DQK, DV>(pf, smem + ((t + 1) & 1) * G::STAGE, tid);
-      __syncthreads();
-      if (t + 2 < ntiles)
-        q_load<DQK, DV>(pf, kb, vb, a.k_stride, a.v_stride, k_lo + (t + 2) * Q_BN, k_last, tid);
-    }
+    pipeline_lds_mfma<4 * G::NQT, 2, kBwdAhead>();
+  };
+
+  if (ntiles > 0) issue(0, ks0, vs0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  auto step = [&](int t, const char* ks, const char* vs, char* kn, char* vn)
+      __attribute__((always_inline)) {
+    if (t + 1 < ntiles) issue(t + 1, kn, vn);
+    tile(t, ks, vs);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, ks0, vs0, ks1, vs1);
+    if (t + 1 < ntiles) step(t + 1, ks1, vs1, ks0, vs0);
   }
   if (!wave_live || !row_ok) return;
 

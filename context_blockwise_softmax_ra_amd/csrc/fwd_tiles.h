@@ -50,22 +50,6 @@ __device__ __forceinline__ int v_off(int row, int byte) {
   return row * VROWB + (v_slot<VROWB>(row, byte >> 4) << 4) + (byte & 15);
 }
 
-// Buffer resource over the rows of one tile (gfx9 descriptor word 3).  The
-// record count is never the limit: every offset stays within 64 rows.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, 0x7fffffff, 0x00020000);
-}
-
-// 16 bytes per lane from the tile at byte offset voff into LDS (lane i writes
-// lds + 16i).  The buffer form (buffer_load_dwordx4 ... lds) is used rather
-// than global_load_lds: the compiler treats an outstanding global (FLAT)
-// load into LDS as an out-of-order LDS access and then drains every LDS
-// read before its first use, which serialises the operand reads of a tile.
-__device__ __forceinline__ void g2lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, char* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff,
-                                           0, 0, 0);
-}
-
 // One wave's share (of NW waves) of the direct global->LDS loads of a K/V
 // tile: per instruction a per-lane byte offset (fixed for the whole launch)
 // from the tile's first key row, and a wave-uniform LDS destination.  K and V

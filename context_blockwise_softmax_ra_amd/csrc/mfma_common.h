@@ -95,6 +95,43 @@ __device__ __forceinline__ int xcd_deal(int b, int nb, int g) {
   return (j / g) * round + x * g + (j % g);
 }
 
+// Buffer resource over the rows of one tile (gfx9 descriptor word 3).  The
+// record count is never the limit: every offset stays within one tile.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+
+// 16 (or 4) bytes per lane from the tile at byte offset voff into LDS (lane i
+// writes lds + 16i, or lds + 4i).  The buffer form (buffer_load ... lds) is
+// used rather than global_load_lds: the compiler treats an outstanding
+// global (FLAT) load into LDS as an out-of-order LDS access and then drains
+// every LDS read before its first use, which serialises the operand reads.
+__device__ __forceinline__ void g2lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff,
+                                           0, 0, 0);
+}
+__device__ __forceinline__ void g2lds4(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff,
+                                           0, 0, 0);
+}
+
+// Orders the instructions of a block of NM matrix-core products, each fed by
+// RPM LDS reads, so that the reads run AHEAD products ahead of the products
+// that consume them (the machine scheduler otherwise tends to issue each
+// read right before its product and wait for it).  Call after the code of
+// the block, inside the same basic block.
+template <int NM, int RPM, int AHEAD>
+__device__ __forceinline__ void pipeline_lds_mfma() {
+  static_assert(AHEAD <= NM, "read-ahead beyond the block");
+  __builtin_amdgcn_sched_group_barrier(0x100, RPM * AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < NM - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group,
 // lane i receives element i%4 of the 8 bytes addressed by lane 4r + i/4,
 // r = 0..3.
@@ -116,6 +153,50 @@ template <int ROWB>
 __device__ __forceinline__ int dual_off(int row, int byte) {
   return row * ROWB + ((((byte >> 4) ^ swz(row))) << 4) + (byte & 15);
 }
+
+// One wave's share (of NW waves) of the direct global->LDS loads of a
+// [ROWS x DIM] bf16 tile into the dual layout with ROWB-byte rows.
+// Instruction j fills LDS bytes [1024 j, 1024 j + 1024); lane i writes the 16
+// bytes at 1024 j + 16 i, i.e. row (1024 j + 16 i) / ROWB at slot s, and
+// fetches the global chunk the swizzle maps to slot s (s ^ swz(row), an
+// involution within each 256-byte half).  Chunks past DIM (row padding up to
+// ROWB) fetch a chunk of the first half instead; they are never read.
+template <int ROWS, int DIM, int ROWB, int NW>
+struct DualLoader {
+  static constexpr int INST = ROWS * ROWB / 1024;
+  static_assert(INST % NW == 0 && DIM >= 128, "tile load split");
+  static constexpr int PER = INST / NW;
+  uint32_t off[PER];  // byte offset of the fetched chunk from the tile's first row
+  int wave, lane;
+
+  __device__ __forceinline__ int row(int jj) const { return ((wave + NW * jj) * 1024 + 16 * lane) / ROWB; }
+  __device__ __forceinline__ int colb(int jj) const {
+    const int slot = (((wave + NW * jj) * 1024 + 16 * lane) % ROWB) >> 4;
+    const int c = slot ^ swz(row(jj));
+    return (c * 16 < DIM * 2 ? c : (c & 15)) * 16;
+  }
+  __device__ __forceinline__ void init(int64_t row_stride_bytes, int w, int l) {
+    wave = w;
+    lane = l;
+#pragma unroll
+    for (int jj = 0; jj < PER; ++jj) off[jj] = (uint32_t)(row(jj) * row_stride_bytes + colb(jj));
+  }
+  // rows_left: rows available from the tile's first row on (the last tile of
+  // a range is clamped to its last row)
+  __device__ __forceinline__ void issue(const void* base, int64_t row_stride_bytes, int rows_left,
+                                        char* lds) const {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(base);
+    if (rows_left >= ROWS) {
+#pragma unroll
+      for (int jj = 0; jj < PER; ++jj) g2lds(r, off[jj], lds + (wave + NW * jj) * 1024);
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < PER; ++jj)
+        g2lds(r, (uint32_t)(min(row(jj), rows_left - 1) * row_stride_bytes + colb(jj)),
+              lds + (wave + NW * jj) * 1024);
+    }
+  }
+};
 
 // Byte column, within a 32-column tile of 16-bit elements, that lane
 // addresses in a transposing read: 16*((lane/16)%2) + 4*(lane%4) elements.
