@@ -86,6 +86,8 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char os1[G::O_BYTES];
   __shared__ __attribute__((aligned(256))) float ld0[2 * KV_BQ];
   __shared__ __attribute__((aligned(256))) float ld1[2 * KV_BQ];
+  // V of the workgroup's 128 keys (dual layout): read as B operands of dP
+  __shared__ __attribute__((aligned(1024))) char vsm[KV_BN * G::OROWB];
 
   int b = xcd_remap(blockIdx.x, gridDim.x);
   const int kt = b % a.n_ktiles;
@@ -107,18 +109,21 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
   const int my_key_rel = wk_rel + l32;               // this lane's key column
   const int my_key = min(k_lo + my_key_rel, k_hi - 1);
 
-  // K, V of this lane's key as B operands (k = dims 16kk + 8g .. +7)
-  bf16x8 kf[G::KK], vf[G::VK];
+  // K of this lane's key as B operands (k = dims 16kk + 8g .. +7); V of the
+  // workgroup's keys goes to LDS (keys past the block re-read the last one)
+  bf16x8 kf[G::KK];
   {
     const __bf16* kp = reinterpret_cast<const __bf16*>(a.k) + (int64_t)my_key * a.k_stride +
                        (int64_t)kvh * DQK + 8 * g;
-    const __bf16* vp = reinterpret_cast<const __bf16*>(a.v) + (int64_t)my_key * a.v_stride +
-                       (int64_t)kvh * DV + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < G::KK; ++kk) kf[kk] = as_bf16x8(ldg16(kp + 16 * kk));
-#pragma unroll
-    for (int kk = 0; kk < G::VK; ++kk) vf[kk] = as_bf16x8(ldg16(vp + 16 * kk));
+    DualLoader<KV_BN, DV, G::OROWB, NT / 64> lvk;
+    const int64_t vsb = a.v_stride * 2;
+    lvk.init(vsb, wave, lane);
+    lvk.issue(reinterpret_cast<const char*>(a.v) + ((int64_t)k0 * a.v_stride + (int64_t)kvh * DV) * 2,
+              vsb, k_hi - k0, vsm);
   }
+  const int vrow = wave * 32 + l32;  // this lane's key row in vsm
   f32x16 dk[G::NQT], dv[G::NVT];
 #pragma unroll
   for (int t = 0; t < G::NQT; ++t) dk[t] = zero16();
@@ -170,16 +175,19 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
       s = mma(as_bf16x8(lds16(qs + dual_off<G::QROWB>(arow, (16 * kk + 8 * g) * 2))), kf[kk], s);
 #pragma unroll
     for (int kk = 0; kk < G::VK; ++kk)
-      dp = mma(as_bf16x8(lds16(os + dual_off<G::OROWB>(arow, (16 * kk + 8 * g) * 2))), vf[kk], dp);
-    pipeline_lds_mfma<G::KK + G::VK, 1, kBwdAhead>();
+      dp = mma(as_bf16x8(lds16(os + dual_off<G::OROWB>(arow, (16 * kk + 8 * g) * 2))),
+               as_bf16x8(lds16(vsm + dual_off<G::OROWB>(vrow, (16 * kk + 8 * g) * 2))), dp);
+    pipeline_lds_mfma_n<G::KK, 1, G::VK, 2, kBwdAhead>();
     __builtin_amdgcn_sched_barrier(0);
     const bool need_mask = (my_key_rel >= klen) || (wk_rel + 31 >= klen) ||
                            (CAUSAL && qt_rel < wk_rel + 31) || (qt_rel + KV_BQ > qlen);
+    // A row that sees nothing (lse = -inf) only occurs in a masked tile:
+    // every pair of an unmasked tile is visible.  Its exp overflows to inf
+    // and the mask then replaces P by 0, so lse needs no guard.
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = 16 * (i >> 3) + 8 * g + (i & 7);
-      const float lr = lsd[r];
-      const float l2 = lr == -INFINITY ? INFINITY : lr * kLog2e;  // rows that see nothing: P = 0
+      const float l2 = lsd[r] * kLog2e;
       const float dl = lsd[KV_BQ + r];
       float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -l2));
       if (need_mask) {

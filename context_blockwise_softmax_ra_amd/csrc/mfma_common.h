@@ -132,6 +132,25 @@ __device__ __forceinline__ void pipeline_lds_mfma() {
   __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
 }
 
+// The same for a block of N1 products fed by R1 reads each followed by N2
+// products fed by R2 reads each.
+template <int N1, int R1, int N2, int R2, int AHEAD>
+__device__ __forceinline__ void pipeline_lds_mfma_n() {
+  static_assert(AHEAD <= N1 && AHEAD <= N2, "read-ahead beyond the block");
+  __builtin_amdgcn_sched_group_barrier(0x100, R1 * AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < N1 - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R1, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < N2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group,
 // lane i receives element i%4 of the 8 bytes addressed by lane 4r + i/4,
 // r = 0..3.
