@@ -280,6 +280,8 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char ks1[G::K_BYTES];
   __shared__ __attribute__((aligned(1024))) char vs0[G::V_BYTES];
   __shared__ __attribute__((aligned(1024))) char vs1[G::V_BYTES];
+  // dO of the workgroup's 128 query rows (dual layout): B operands of dP^T
+  __shared__ __attribute__((aligned(1024))) char osm[Q_BM * G::VROWB];
 
   int b = xcd_remap(blockIdx.x, gridDim.x);
   const int hg = b % a.group;
@@ -314,17 +316,21 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a) {
   const int ntiles = (kend + Q_BN - 1) / Q_BN;
 
   const int row = min(my_row, q_hi - 1);
-  bf16x8 qf[G::KK], of[G::VK];
+  // Q of this lane's row as B operands (k = dims 16kk + 8g .. +7); dO of the
+  // workgroup's rows goes to LDS (rows past the part re-read the last one)
+  bf16x8 qf[G::KK];
   {
     const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + (int64_t)row * a.q_stride +
                        (int64_t)h * DQK + 8 * g;
-    const __bf16* op = reinterpret_cast<const __bf16*>(a.dout) + ((int64_t)row * a.hq + h) * DV +
-                       8 * g;
 #pragma unroll
     for (int kk = 0; kk < G::KK; ++kk) qf[kk] = as_bf16x8(ldg16(qp + 16 * kk));
-#pragma unroll
-    for (int kk = 0; kk < G::VK; ++kk) of[kk] = as_bf16x8(ldg16(op + 16 * kk));
+    DualLoader<Q_BM, DV, G::VROWB, NT / 64> lod;
+    const int64_t osb = (int64_t)a.hq * DV * 2;
+    lod.init(osb, wave, lane);
+    lod.issue(reinterpret_cast<const char*>(a.dout) + ((int64_t)q0 * a.hq + h) * DV * 2, osb,
+              q_hi - q0, osm);
   }
+  const int orow = wave * 32 + l32;  // this lane's query row in osm
   const int64_t li = (int64_t)h * a.total_q + row;
   const float l2 = lse_log2(a.lse_in, li, row_ok);
   const float dl = row_ok ? a.delta[li] : 0.f;
@@ -363,8 +369,9 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a) {
         s = mma(as_bf16x8(lds16(ks + dual_off<G::KROWB>(kr, (16 * kk + 8 * g) * 2))), qf[kk], s);
 #pragma unroll
       for (int kk = 0; kk < G::VK; ++kk)
-        dp = mma(as_bf16x8(lds16(vs + dual_off<G::VROWB>(kr, (16 * kk + 8 * g) * 2))), of[kk], dp);
-      pipeline_lds_mfma<G::KK + G::VK, 1, kBwdAhead>();
+        dp = mma(as_bf16x8(lds16(vs + dual_off<G::VROWB>(kr, (16 * kk + 8 * g) * 2))),
+                 as_bf16x8(lds16(osm + dual_off<G::VROWB>(orow, (16 * kk + 8 * g) * 2))), dp);
+      pipeline_lds_mfma_n<G::KK, 1, G::VK, 2, kBwdAhead>();
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
