@@ -11,11 +11,13 @@
 // exactly as in the forward).  Two launches, no atomics, deterministic:
 //
 // dK/dV kernel -- workgroup = 128 keys of one kv head (4 waves x 32 keys).
-//   K and V of the wave's keys stay in registers; the loop walks every
+//   K of the wave's keys stays in registers, V of the workgroup's keys in
+//   LDS (loaded once); the loop walks every
 //   query head of the kv group and every 32-row query tile of the segment
 //   part (causal: only tiles at or below the keys).  Per tile, with lane l
 //   owning key column l%32 of the 32x32 accumulators:
-//     S  = Q K^T, dP = dO V^T        A = Q / dO rows from LDS, B = K / V regs
+//     S  = Q K^T, dP = dO V^T        A = Q / dO rows from LDS, B = K regs /
+//                                    V rows from LDS
 //     dV += P^T dO, dK += dS^T Q     A = P^T / dS^T straight from the S / dP
 //                                    accumulators (query rows fed in the
 //                                    permuted order sigma so 8 consecutive
@@ -24,7 +26,8 @@
 // dQ kernel -- workgroup = 128 query rows of one head (4 waves x 32 rows),
 //   the forward's shape: lane l owns query row l%32; per 64-key tile
 //     S^T = K Q^T, dP^T = V dO^T     A = K / V rows from LDS (sigma order),
-//                                    B = Q / dO held in registers
+//                                    B = Q held in registers / dO rows of
+//                                    the workgroup in LDS (loaded once)
 //     dQ^T += K^T dS^T               A = K via transposing LDS reads.
 // Q, dO and K tiles are read both by 128-bit row reads and by transposing
 // reads, so they use the XOR-swizzled "dual" LDS layout (conflict-free for
