@@ -495,6 +495,10 @@ def main():
         "per_rank": {
             "ms": [round(x, 4) for x in rank_ms],
             "pairs_x_heads": [int(sum(p for (p, _, _) in work[r])) for r in range(C)],
+            "tflops": [round(sum(p for (p, _, _) in work[r]) * fl_pair / (rank_ms[r] / 1e3) / 1e12, 2)
+                       for r in range(C)],
+            "tiles_visited": [int(sum(t for (_, t, _) in work[r])) for r in range(C)],
+            "tiles_skipped": [int(sum(t for (_, _, t) in work[r])) for r in range(C)],
             "slowest_rank": max(range(C), key=lambda r: rank_ms[r]),
             "time_max_over_mean": round(max(rank_ms) / (sum(rank_ms) / C), 4),
         },
