@@ -34,6 +34,10 @@
  *     never allocates device memory.  Work is queued on the caller's stream
  *     (a hipStream_t passed as void*; NULL = the null stream); buffers must
  *     outlive the queued work.
+ *   - Empty work: zero-length segments, and descriptors whose segments are
+ *     all empty, are valid; then nothing is launched for them.  Buffer
+ *     pointers must still be non-NULL (any valid address will do when a
+ *     buffer's size is zero).
  *   - Errors: arguments are validated before anything is queued; on
  *     RA_ERR_INVALID_ARG / RA_ERR_UNSUPPORTED nothing is launched and
  *     nothing is written.  A failed launch returns RA_ERR_HIP.  Faults of

@@ -160,6 +160,41 @@ def test_block_fwd_fp32_edge_cases(case):
     assert (out[~cov] == 7.0).all()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_all_empty_segments_are_a_no_op(dtype, monkeypatch):
+    """Segments that are all empty (the degenerate batch): every call succeeds
+    and writes nothing.  The buffers hold one token, the segments none."""
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    d = 128 if dtype == "bf16" else 64
+    cu = np.array([0, 0, 0], np.int32)
+    cud = torch.from_numpy(cu).to(DEV)
+    q = torch.ones(1, 2, d, dtype=tdt, device=DEV)
+    k = torch.ones(1, 1, d, dtype=tdt, device=DEV)
+    v = torch.ones(1, 1, d, dtype=tdt, device=DEV)
+    out = torch.full((1, 2, d), 7.0, device=DEV)
+    lse = torch.full((2, 1), 7.0, device=DEV)
+    for kernel in (KERNELS if dtype == "bf16" else ("4w",)):
+        monkeypatch.setenv("RA_FWD_KERNEL", kernel)
+        for causal in (False, True):
+            desc = L.attn_desc(q, k, v, cud, cud, cu, cu, causal=causal)
+            L.ra_block_attn_fwd(desc, out, lse)
+            L.ra_block_attn_fwd_merge(desc, out, lse)
+    L.ra_lse_merge(out, lse, out.clone(), lse.clone(), cud, cu, 0)
+    if dtype == "bf16":
+        desc = L.attn_desc(q, k, v, cud, cud, cu, cu, causal=True)
+        do = torch.ones(1, 2, d, dtype=tdt, device=DEV)
+        delta = torch.full((2, 1), 7.0, device=DEV)
+        dq = torch.full((1, 2, d), 7.0, device=DEV)
+        dk = torch.full((1, 1, d), 7.0, device=DEV)
+        dv = torch.full((1, 1, d), 7.0, device=DEV)
+        L.ra_block_attn_bwd(desc, do, lse, delta, dq, dk, dv)
+        torch.cuda.synchronize()
+        for t in (dq, dk, dv):
+            assert (t == 7.0).all()
+    torch.cuda.synchronize()
+    assert (out == 7.0).all() and (lse == 7.0).all()
+
+
 # ---------------------------------------------------------------------------
 # bandwidth kernels
 # ---------------------------------------------------------------------------
