@@ -61,10 +61,53 @@ def parse():
     ap.add_argument("--backward", type=int, default=0,
                     help="1: time the backward shares (after one forward) instead; for the "
                          "256K MLA workload")
+    ap.add_argument("--merge", type=int, default=0,
+                    help="1: time ra_lse_merge alone on the workload's full-row step (every "
+                         "local row, every query head, fp32 partials) and report HBM GB/s")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB 3 times (the "
                          "reference kernel that scales HBM byte counters), then exit")
     return ap.parse_args()
+
+
+def bench_merge(a, w, torch, L):
+    """ra_lse_merge on one full-row step of a rank share: HBM-bound, in GB/s."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    T = w.seqlen // w.cp                        # local rows of a rank share
+    cu = np.array([0, T], np.int32)
+    cud = torch.from_numpy(cu).to(dev)
+    g = torch.Generator(device=dev).manual_seed(11)
+    oa = torch.randn((T, w.hq, w.dv), generator=g, device=dev)
+    ob = torch.randn((T, w.hq, w.dv), generator=g, device=dev)
+    la = torch.randn((w.hq, T), generator=g, device=dev)
+    lb = torch.randn((w.hq, T), generator=g, device=dev)
+    for _ in range(a.warmup):
+        L.ra_lse_merge(oa, la, ob, lb, cud, cu, 0)
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(a.steps):
+        L.ra_lse_merge(oa, la, ob, lb, cud, cu, 0)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / a.steps
+    nbytes = T * w.hq * (12 * w.dv + 12)       # read both partials and lses, write acc + lse
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {
+        "metric": "lse merge HBM GB/s (one full-row step of a rank share, fp32 partials), 1 GPU",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded N(0,1))",
+        "config": {"workload": f"{w.name}: ra_lse_merge of {T} rows x {w.hq} heads x dv {w.dv}",
+                   "bytes_per_merge": nbytes},
+        "roofline": {"bound": "hbm", "kernel": "lse_merge_kernel", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
 
 
 def copy_calibration(mib: int):
@@ -355,6 +398,9 @@ def main():
     w = synth.WORKLOADS[a.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if a.merge:
+        print(json.dumps(bench_merge(a, w, torch, L)), flush=True)
+        return
     print(f"# workload {w.name}: S={w.seqlen} CP={w.cp} hq={w.hq} hkv={w.hkv} "
           f"d={w.dqk}/{w.dv} {w.dtype}", file=sys.stderr, flush=True)
     q = synth.cast(w.q(), w.dtype).to(dev)
