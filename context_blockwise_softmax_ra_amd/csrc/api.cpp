@@ -693,6 +693,18 @@ ra_status ra_attn_bwd_delta(const void* out, ra_dtype out_dtype, const void* dou
   return ok();
 }
 
+// dK/dV workgroups: 128 keys each, or (d_qk = 128) 32 keys with the query
+// iterations split over the workgroup's waves when 128-key workgroups would
+// not give every CU one (history blocks of GQA/MHA rank shares).
+// RA_BWD_KV_SPLIT=0 or =1 in the environment forces one.
+static bool bwd_kv_split(const ra_attn_desc* d, const ra::AttnArgs& a) {
+  if (d->dqk != 128) return false;
+  const char* e = std::getenv("RA_BWD_KV_SPLIT");
+  if (e && !std::strcmp(e, "1")) return true;
+  if (e && !std::strcmp(e, "0")) return false;
+  return (long long)a.n_seq * a.hkv * a.n_ktiles < 256;
+}
+
 static ra_status launch_bwd(const ra_attn_desc* d, const Checked& c, const void* dout,
                             const float* lse, const float* delta, float* dq, float* dk, float* dv,
                             hipStream_t st) {
@@ -704,7 +716,8 @@ static ra_status launch_bwd(const ra_attn_desc* d, const Checked& c, const void*
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  hipError_t e = ra::launch_attn_bwd_bf16(a, d->dqk, d->dv, d->causal != 0, st);
+  hipError_t e =
+      ra::launch_attn_bwd_bf16(a, d->dqk, d->dv, d->causal != 0, bwd_kv_split(d, a), st);
   if (e == hipErrorInvalidValue) return fail(RA_ERR_UNSUPPORTED, "backward variant not built");
   if (e != hipSuccess) return hip_fail(e, "attention backward launch");
   return RA_OK;

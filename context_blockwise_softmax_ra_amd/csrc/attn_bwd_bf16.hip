@@ -79,18 +79,27 @@ struct GeoKV {
   static_assert(DV == 128, "dO rows are 256 bytes");
 };
 
-template <int DQK, int DV, bool CAUSAL>
+// QS ("query split"): a workgroup covers 32 keys and its 4 waves split the
+// (query head, query tile) iterations among themselves, each with its own
+// two LDS stages and no barrier in the loop; the waves' dK/dV are added in
+// a fixed order (wave 0 + 1 + 2 + 3) through LDS at the end, so the result
+// stays deterministic.  It gives 4x the workgroups of the 128-key form, for
+// launches with few key tiles (GQA/MHA history blocks at d_qk = 128).
+template <int DQK, int DV, bool CAUSAL, bool QS>
 __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
   using G = GeoKV<DQK, DV>;
+  constexpr int KBN = QS ? 32 : KV_BN;  // keys per workgroup
+  constexpr int NS = QS ? NT / 64 : 1;  // stage sets (one per wave with QS)
+  static_assert(!QS || (G::Q_BYTES == 8192 && G::O_BYTES == 8192), "QS reduction buffers");
   // per stage: Q tile, dO tile, lse (rows 0..31) and delta (32..63)
-  __shared__ __attribute__((aligned(1024))) char qs0[G::Q_BYTES];
-  __shared__ __attribute__((aligned(1024))) char qs1[G::Q_BYTES];
-  __shared__ __attribute__((aligned(1024))) char os0[G::O_BYTES];
-  __shared__ __attribute__((aligned(1024))) char os1[G::O_BYTES];
-  __shared__ __attribute__((aligned(256))) float ld0[2 * KV_BQ];
-  __shared__ __attribute__((aligned(256))) float ld1[2 * KV_BQ];
-  // V of the workgroup's 128 keys (dual layout): read as B operands of dP
-  __shared__ __attribute__((aligned(1024))) char vsm[KV_BN * G::OROWB];
+  __shared__ __attribute__((aligned(1024))) char qs0[NS][G::Q_BYTES];
+  __shared__ __attribute__((aligned(1024))) char qs1[NS][G::Q_BYTES];
+  __shared__ __attribute__((aligned(1024))) char os0[NS][G::O_BYTES];
+  __shared__ __attribute__((aligned(1024))) char os1[NS][G::O_BYTES];
+  __shared__ __attribute__((aligned(256))) float ld0[NS][2 * KV_BQ];
+  __shared__ __attribute__((aligned(256))) float ld1[NS][2 * KV_BQ];
+  // V of the workgroup's keys (dual layout): read as B operands of dP
+  __shared__ __attribute__((aligned(1024))) char vsm[KBN * G::OROWB];
 
   int b = xcd_remap(blockIdx.x, gridDim.x);
   const int kt = b % a.n_ktiles;
@@ -101,13 +110,14 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
   int q_lo, q_hi, k_lo, k_hi;
   part_range(a.cu_q[seg], a.cu_q[seg + 1], a.q_part, &q_lo, &q_hi);
   part_range(a.cu_k[seg], a.cu_k[seg + 1], a.k_part, &k_lo, &k_hi);
-  const int k0 = k_lo + kt * KV_BN;
+  const int k0 = k_lo + kt * KBN;
   const int qlen = q_hi - q_lo, klen = k_hi - k_lo;
   if (k0 >= k_hi || qlen <= 0) return;
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
-  const int wk_rel = kt * KV_BN + wave * 32;        // first key of the wave (part-relative)
+  const int ws = QS ? wave : 0;                      // this wave's stage set
+  const int wk_rel = kt * KBN + (QS ? 0 : wave * 32);  // first key of the wave (part-relative)
   const bool wave_live = wk_rel < klen;
   const int my_key_rel = wk_rel + l32;               // this lane's key column
   const int my_key = min(k_lo + my_key_rel, k_hi - 1);
@@ -120,13 +130,13 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
                        (int64_t)kvh * DQK + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < G::KK; ++kk) kf[kk] = as_bf16x8(ldg16(kp + 16 * kk));
-    DualLoader<KV_BN, DV, G::OROWB, NT / 64> lvk;
+    DualLoader<KBN, DV, G::OROWB, NT / 64> lvk;
     const int64_t vsb = a.v_stride * 2;
     lvk.init(vsb, wave, lane);
     lvk.issue(reinterpret_cast<const char*>(a.v) + ((int64_t)k0 * a.v_stride + (int64_t)kvh * DV) * 2,
               vsb, k_hi - k0, vsm);
   }
-  const int vrow = wave * 32 + l32;  // this lane's key row in vsm
+  const int vrow = (QS ? 0 : wave * 32) + l32;  // this lane's key row in vsm
   f32x16 dk[G::NQT], dv[G::NVT];
 #pragma unroll
   for (int t = 0; t < G::NQT; ++t) dk[t] = zero16();
@@ -134,7 +144,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
   for (int t = 0; t < G::NVT; ++t) dv[t] = zero16();
 
   const int n_qt = (qlen + KV_BQ - 1) / KV_BQ;
-  const int qt_begin = CAUSAL ? (kt * KV_BN) / KV_BQ : 0;
+  const int qt_begin = CAUSAL ? (kt * KBN) / KV_BQ : 0;
   const int per_head = n_qt - qt_begin;
   const int n_it = per_head > 0 ? per_head * a.group : 0;
   const float c2 = a.scale_log2;
@@ -143,11 +153,12 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
 
   auto it_head = [&](int it) { return kvh * a.group + it / per_head; };
   auto it_q0 = [&](int it) { return q_lo + (qt_begin + it % per_head) * KV_BQ; };
-  DualLoader<KV_BQ, DQK, G::QROWB, NT / 64> lq;
-  DualLoader<KV_BQ, DV, G::OROWB, NT / 64> lo;
+  // with QS each wave loads its own tiles alone
+  DualLoader<KV_BQ, DQK, G::QROWB, QS ? 1 : NT / 64> lq;
+  DualLoader<KV_BQ, DV, G::OROWB, QS ? 1 : NT / 64> lo;
   const int64_t qsb = a.q_stride * 2, osb = (int64_t)a.hq * DV * 2;
-  lq.init(qsb, wave, lane);
-  lo.init(osb, wave, lane);
+  lq.init(qsb, QS ? 0 : wave, lane);
+  lo.init(osb, QS ? 0 : wave, lane);
   // tile it's Q, dO, lse and delta into one stage (rows past the part are
   // clamped to its last row here and masked in the products)
   auto issue = [&](int it, char* qd, char* od, float* ldd) __attribute__((always_inline)) {
@@ -156,7 +167,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
              qsb, rows_left, qd);
     lo.issue(reinterpret_cast<const char*>(a.dout) + ((int64_t)q0 * a.hq + h) * DV * 2, osb,
              rows_left, od);
-    if (wave == 0) {
+    if (QS || wave == 0) {
       const uint32_t r4 = (uint32_t)min(lane & (KV_BQ - 1), rows_left - 1) * 4;
       const int64_t i0 = (int64_t)h * a.total_q + q0;
       if (lane < KV_BQ) g2lds4(tile_rsrc(a.lse_in + i0), r4, ldd);
@@ -226,20 +237,73 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
     pipeline_lds_mfma<2 * (G::NVT + G::NQT), 2, kBwdAhead>();
   };
 
-  if (n_it > 0) issue(0, qs0, os0, ld0);
+  // iterations of this wave: all (it += 1), or with QS every 4th from the
+  // wave's index
+  const int it0 = QS ? wave : 0, istep = QS ? NT / 64 : 1;
+  if (it0 < n_it) issue(it0, qs0[ws], os0[ws], ld0[ws]);
   __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  __syncthreads();  // V (and, without QS, the first tile) in LDS
   auto step = [&](int it, const char* qs, const char* os, const float* lsd, char* qn, char* on,
                   float* ln) __attribute__((always_inline)) {
-    if (it + 1 < n_it) issue(it + 1, qn, on, ln);
+    if (it + istep < n_it) issue(it + istep, qn, on, ln);
     tile(it, qs, os, lsd);
-    // next tile landed (own loads) and every wave is done with this one
+    // next tile landed (own loads); without QS also every wave is done with
+    // this one (with QS the stages are the wave's own, and its reads of
+    // them complete before it issues the next load into them)
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    if (!QS) __syncthreads();
   };
-  for (int it = 0; it < n_it; it += 2) {
-    step(it, qs0, os0, ld0, qs1, os1, ld1);
-    if (it + 1 < n_it) step(it + 1, qs1, os1, ld1, qs0, os0, ld0);
+  for (int it = it0; it < n_it; it += 2 * istep) {
+    step(it, qs0[ws], os0[ws], ld0[ws], qs1[ws], os1[ws], ld1[ws]);
+    if (it + istep < n_it) step(it + istep, qs1[ws], os1[ws], ld1[ws], qs0[ws], os0[ws], ld0[ws]);
+  }
+  if (QS) {
+    // add the waves' dK/dV in a fixed order: waves 1..3 park theirs in their
+    // own (now idle) stage buffers, wave 0 adds them one by one
+    __syncthreads();
+    if (wave > 0) {
+      float* pk0 = reinterpret_cast<float*>(qs0[wave]);
+      float* pk1 = reinterpret_cast<float*>(qs1[wave]);
+      float* pv0 = reinterpret_cast<float*>(os0[wave]);
+      float* pv1 = reinterpret_cast<float*>(os1[wave]);
+#pragma unroll
+      for (int nt = 0; nt < G::NQT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int e = nt * 16 + i;  // 64 floats per lane, lane-major
+          (e < 32 ? pk0 : pk1)[(e & 31) * 64 + lane] = dk[nt][i];
+        }
+#pragma unroll
+      for (int nt = 0; nt < G::NVT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int e = nt * 16 + i;
+          (e < 32 ? pv0 : pv1)[(e & 31) * 64 + lane] = dv[nt][i];
+        }
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) {
+      const float* pk0 = reinterpret_cast<const float*>(qs0[w]);
+      const float* pk1 = reinterpret_cast<const float*>(qs1[w]);
+      const float* pv0 = reinterpret_cast<const float*>(os0[w]);
+      const float* pv1 = reinterpret_cast<const float*>(os1[w]);
+#pragma unroll
+      for (int nt = 0; nt < G::NQT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int e = nt * 16 + i;
+          dk[nt][i] += (e < 32 ? pk0 : pk1)[(e & 31) * 64 + lane];
+        }
+#pragma unroll
+      for (int nt = 0; nt < G::NVT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int e = nt * 16 + i;
+          dv[nt][i] += (e < 32 ? pv0 : pv1)[(e & 31) * 64 + lane];
+        }
+    }
   }
   if (!wave_live) return;
 
@@ -440,28 +504,37 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a) {
 
 }  // namespace
 
-hipError_t launch_attn_bwd_bf16(const AttnArgs& a0, int dqk, int dv, bool causal,
+hipError_t launch_attn_bwd_bf16(const AttnArgs& a0, int dqk, int dv, bool causal, bool kv_split,
                                 hipStream_t st) {
-  // a0.n_qtiles counts 128-row query tiles, a0.n_ktiles 128-key tiles
+  // a0.n_qtiles counts 128-row query tiles, a0.n_ktiles 128-key tiles; with
+  // kv_split (d_qk = 128 only) the dK/dV kernel runs 32-key workgroups
   AttnArgs a = a0;
   const long long nq = (long long)a.n_seq * a.hkv * a.n_qtiles * a.group;
-  const long long nk = (long long)a.n_seq * a.hkv * a.n_ktiles;
+  AttnArgs ak = a;
+  if (kv_split) ak.n_ktiles = 4 * a.n_ktiles;
+  const long long nk = (long long)a.n_seq * a.hkv * ak.n_ktiles;
   if (nq > 0x7fffffffLL || nk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-#define RA_BWD_LAUNCH(DQ, DVV, C)                                                              \
+  if (kv_split && dqk != 128) return hipErrorInvalidValue;
+#define RA_BWD_LAUNCH(DQ, DVV, C, QSPLIT)                                                      \
   do {                                                                                         \
     if (nq > 0)                                                                                \
       hipLaunchKernelGGL((attn_bwd_dq_kernel<DQ, DVV, C>), dim3((unsigned)nq), dim3(NT), 0, st, \
                          a);                                                                   \
     if (nk > 0)                                                                                \
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQ, DVV, C>), dim3((unsigned)nk), dim3(NT), 0,   \
-                         st, a);                                                               \
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQ, DVV, C, QSPLIT>), dim3((unsigned)nk),       \
+                         dim3(NT), 0, st, ak);                                                 \
   } while (0)
   if (dqk == 128 && dv == 128) {
-    if (causal) RA_BWD_LAUNCH(128, 128, true);
-    else RA_BWD_LAUNCH(128, 128, false);
+    if (kv_split) {
+      if (causal) RA_BWD_LAUNCH(128, 128, true, true);
+      else RA_BWD_LAUNCH(128, 128, false, true);
+    } else {
+      if (causal) RA_BWD_LAUNCH(128, 128, true, false);
+      else RA_BWD_LAUNCH(128, 128, false, false);
+    }
   } else if (dqk == 192 && dv == 128) {
-    if (causal) RA_BWD_LAUNCH(192, 128, true);
-    else RA_BWD_LAUNCH(192, 128, false);
+    if (causal) RA_BWD_LAUNCH(192, 128, true, false);
+    else RA_BWD_LAUNCH(192, 128, false, false);
   } else {
     return hipErrorInvalidValue;
   }

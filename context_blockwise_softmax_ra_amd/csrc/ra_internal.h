@@ -98,7 +98,7 @@ hipError_t launch_zigzag_copy(const void* src, void* dst, int64_t row_bytes, int
 hipError_t launch_bwd_delta(const void* out, int out_dtype, const void* dout, int dout_dtype,
                             int32_t total_t, int32_t hq, int32_t dv, float* delta,
                             hipStream_t st);
-hipError_t launch_attn_bwd_bf16(const AttnArgs& a, int dqk, int dv, bool causal,
+hipError_t launch_attn_bwd_bf16(const AttnArgs& a, int dqk, int dv, bool causal, bool kv_split,
                                 hipStream_t st);
 
 }  // namespace ra

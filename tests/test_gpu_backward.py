@@ -63,12 +63,16 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("split", ["0", "1"])
 @pytest.mark.parametrize("dims", [(128, 128), (192, 128)])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_block_bwd_edge_cases(case, dims):
+def test_block_bwd_edge_cases(case, dims, split, monkeypatch):
     name, lq, lk, qp, kp, causal, hq, hkv = case
     dqk, dv = dims
-    log(f"case {name} dims {dims}")
+    if split == "1" and dqk != 128:
+        pytest.skip("the query-split dK/dV form is built for d_qk = 128")
+    monkeypatch.setenv("RA_BWD_KV_SPLIT", split)
+    log(f"case {name} dims {dims} dK/dV query split {split}")
     cu_q, cu_k = synth.cu_seqlens(lq), synth.cu_seqlens(lk)
     g = torch.Generator().manual_seed(11 + len(name) + dqk)
     Tq, Tk = int(cu_q[-1]), int(cu_k[-1])
@@ -184,7 +188,10 @@ def test_mla_backward_reduced_full_parity():
     _full_bwd_parity(synth.reduced("mla_256k", 4096, 8))
 
 
-def test_gqa_backward_reduced_full_parity():
+@pytest.mark.parametrize("split", ["auto", "0", "1"])
+def test_gqa_backward_reduced_full_parity(split, monkeypatch):
+    if split != "auto":
+        monkeypatch.setenv("RA_BWD_KV_SPLIT", split)
     _full_bwd_parity(synth.reduced("gqa_32k", 4096, 8))
 
 
