@@ -551,6 +551,24 @@ ra_status ra_cast_f32_bf16(const float* src, void* dst, int64_t n, void* stream)
   return ok();
 }
 
+// KV split of a fused rank share: a launch of the 4-wave kernel with fewer
+// than 256 workgroups (a rank share of few rows and heads) leaves CUs idle,
+// so its blocks are dealt round-robin over `split` parts (more workgroups),
+// each writing a float32 partial, and a combine kernel weights the parts by
+// their lse.  RA_FWD_KV_SPLIT=<n> in the environment forces n parts (1 =
+// none).
+static int fwd_kv_split(const ra_rank_desc* d, const Checked& c) {
+  const ra_attn_desc& L = d->local;
+  if (d->fuse_merge != 2 || L.dtype != RA_BF16 || d->cp_size <= 1) return 1;
+  if (use_pingpong(&L, RA_PART_ALL)) return 1;
+  const char* e = std::getenv("RA_FWD_KV_SPLIT");
+  if (e && *e) return std::max(1, std::min(std::atoi(e), (int)d->cp_size));
+  const long long wg = (long long)L.n_seq * L.hkv * (L.hq / L.hkv) *
+                       ((c.max_q_part + ra::kFwdBlockM - 1) / ra::kFwdBlockM);
+  if (wg <= 0 || wg >= 256) return 1;
+  return (int)std::min<long long>(d->cp_size, (512 + wg - 1) / wg);
+}
+
 ra_status ra_rank_forward_workspace(const ra_rank_desc* d, size_t* bytes) {
   if (!d || !bytes) return fail(RA_ERR_INVALID_ARG, "NULL argument");
   Checked c;
@@ -560,7 +578,10 @@ ra_status ra_rank_forward_workspace(const ra_rank_desc* d, size_t* bytes) {
   const size_t lse_b = align256((size_t)c.total_q * d->local.hq * sizeof(float));
   size_t b = 0;
   if (d->fuse_merge == 2 && d->local.dtype == RA_BF16) {
-    *bytes = 0;  // one launch, output written directly
+    // one launch writing the output directly, or with a KV split the
+    // float32 partials of every part
+    const int split = fwd_kv_split(d, c);
+    *bytes = split > 1 ? (size_t)split * (out_b + lse_b) : 0;
     return ok();
   }
   if (d->out_dtype != RA_FP32) b += out_b;                   // fp32 accumulator
@@ -612,14 +633,32 @@ ra_status ra_rank_forward(const ra_rank_desc* d, void* stream) {
     ra::AttnArgs a = make_args(&sd, cs);
     a.out = static_cast<float*>(d->out);
     a.lse = d->lse;
+    const int split = fwd_kv_split(d, c);
+    rk.split = split;
+    const size_t out_b = align256((size_t)c.total_q * L.hq * L.dv * sizeof(float));
+    const size_t lse_b = align256((size_t)c.total_q * L.hq * sizeof(float));
+    if (split > 1) {
+      // parts: split float32 outputs, then split lse arrays
+      rk.part_out_stride = (int64_t)(out_b / sizeof(float));
+      rk.part_lse_stride = (int64_t)(lse_b / sizeof(float));
+      a.out = static_cast<float*>(d->workspace);
+      a.lse = reinterpret_cast<float*>(static_cast<char*>(d->workspace) + split * out_b);
+    }
     if (d->events && d->events[0] &&
         (e = hipEventRecord((hipEvent_t)d->events[0], hs)) != hipSuccess)
       return hip_fail(e, "event record");
     if (a.n_qtiles > 0) {
       e = use_pingpong(&L, RA_PART_ALL)
               ? ra::launch_rank_fwd_pp(a, rk, L.dqk, L.dv, d->out_dtype == RA_BF16, hs)
-              : ra::launch_rank_fwd_bf16(a, rk, L.dqk, L.dv, d->out_dtype == RA_BF16, hs);
+              : ra::launch_rank_fwd_bf16(a, rk, L.dqk, L.dv,
+                                         split == 1 && d->out_dtype == RA_BF16, hs);
       if (e != hipSuccess) return hip_fail(e, "rank forward launch");
+      if (split > 1) {
+        e = ra::launch_split_combine(a.out, a.lse, split, rk.part_out_stride,
+                                     rk.part_lse_stride, d->out, d->out_dtype, d->lse,
+                                     c.total_q, L.hq, L.dv, hs);
+        if (e != hipSuccess) return hip_fail(e, "split combine launch");
+      }
     }
     if (d->events && d->events[1] &&
         (e = hipEventRecord((hipEvent_t)d->events[1], hs)) != hipSuccess)

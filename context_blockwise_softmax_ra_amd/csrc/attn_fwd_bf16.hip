@@ -84,7 +84,9 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
   const int qt_rev = b % a.n_qtiles;
   b /= a.n_qtiles;
   const int kvh = b % a.hkv;
-  const int seg = b / a.hkv;
+  b /= a.hkv;
+  const int seg = MODE == 2 ? b % a.n_seq : b;
+  const int kv_part = MODE == 2 ? b / a.n_seq : 0;  // part of a KV-split rank share
   // heaviest query tiles first (causal: later rows see more keys; rank share:
   // second-half rows also see the blocks of later ranks)
   const int qt = MODE != 0 ? (a.n_qtiles - 1 - qt_rev) : qt_rev;
@@ -123,14 +125,18 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
   const int my_row = wq0 + l32;
   const int my_row_rel = my_row - q_lo;
   const int64_t ks_bytes = a.k_stride * 2, vs_bytes = a.v_stride * 2;
-  const int nblocks = MODE == 2 ? rk.cp : 1;
+  // blocks of this workgroup: a rank share's blocks kv_part, kv_part +
+  // split, ... (all of them without a split), or the one block
+  const int kv_split = MODE == 2 ? max(rk.split, 1) : 1;
+  const int nblocks = MODE == 2 ? (rk.cp - kv_part + kv_split - 1) / kv_split : 1;
 
-  // block bi of this workgroup, with the number of key tiles it visits
-  auto get_block = [&](int bi) -> Block {
+  // block li of this workgroup, with the number of key tiles it visits
+  auto get_block = [&](int li) -> Block {
     Block blk;
     const void* kp;
     const void* vp;
     int kpart;
+    const int bi = kv_part + li * kv_split;  // ring step of the block
     if (MODE == 2) {
       const int owner = (rk.rank - bi + rk.cp) % rk.cp;
       kp = rk.k[owner];
@@ -342,10 +348,12 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
   const float lse =
       empty ? -INFINITY : (m_fin * a.scale + __builtin_amdgcn_logf(l_tot) * 0.69314718055994531f);
 
-  float* lrow = a.lse + (int64_t)h * a.total_q + my_row;
+  float* const out_base = a.out + (MODE == 2 ? kv_part * rk.part_out_stride : 0);
+  float* lrow = a.lse + (MODE == 2 ? kv_part * rk.part_lse_stride : 0) + (int64_t)h * a.total_q +
+                my_row;
   if (OUT_BF16) {
     // final output straight to bf16 (round to nearest even)
-    unsigned short* orow = reinterpret_cast<unsigned short*>(a.out) + ((int64_t)my_row * a.hq + h) * DV;
+    unsigned short* orow = reinterpret_cast<unsigned short*>(out_base) + ((int64_t)my_row * a.hq + h) * DV;
 #pragma unroll
     for (int tt = 0; tt < G::OT; ++tt)
 #pragma unroll
@@ -357,7 +365,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
       }
     if (g == 0) *lrow = lse;
   } else if (!MERGE) {
-    float* orow = a.out + ((int64_t)my_row * a.hq + h) * DV;
+    float* orow = out_base + ((int64_t)my_row * a.hq + h) * DV;
 #pragma unroll
     for (int tt = 0; tt < G::OT; ++tt)
 #pragma unroll
@@ -371,7 +379,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
       }
     if (g == 0) *lrow = lse;
   } else {
-    float* orow = a.out + ((int64_t)my_row * a.hq + h) * DV;
+    float* orow = out_base + ((int64_t)my_row * a.hq + h) * DV;
     const float la = *lrow;
     const float mm = fmaxf(la, lse);
     const bool both_empty = (mm == -INFINITY);
@@ -400,7 +408,9 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
 template <int DQK, int DV>
 hipError_t launch_t(const AttnArgs& a, const RankKV* rk, bool causal, bool merge, bool out_bf16,
                     hipStream_t st) {
-  const long long nblk = (long long)a.n_seq * a.hkv * a.n_qtiles * a.group;
+  const int split = rk ? max(rk->split, 1) : 1;
+  if (rk && split > 1 && out_bf16) return hipErrorInvalidValue;  // parts are float32
+  const long long nblk = (long long)a.n_seq * a.hkv * a.n_qtiles * a.group * split;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)nblk), block(NT);

@@ -181,6 +181,58 @@ __global__ __launch_bounds__(NT) void bwd_delta_kernel(const void* __restrict__ 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Combine of a KV-split rank share: the same lse weighting as the merge
+// above, over `split` partials at once (weights exp(lse_p - max), summed in
+// part order, so the result is deterministic).  One thread per 4 output
+// dims of a (token, head) row; the thread of dims 0..3 writes the lse.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NT) void split_combine_kernel(
+    const float* __restrict__ part_out, const float* __restrict__ part_lse, int split,
+    int64_t po, int64_t pl, void* __restrict__ out, int out_bf16, float* __restrict__ lse,
+    int32_t total_t, int32_t h, int32_t dv4, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * NT) {
+    const int64_t row = i / dv4;          // token * h + head
+    const int c4 = (int)(i - row * dv4);
+    const int64_t t = row / h;
+    const int hh = (int)(row - t * h);
+    const int64_t li = (int64_t)hh * total_t + t;
+    float m = -INFINITY;
+    for (int p = 0; p < split; ++p) m = fmaxf(m, part_lse[p * pl + li]);
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+    if (m != -INFINITY) {
+      for (int p = 0; p < split; ++p) {
+        const float lp = part_lse[p * pl + li];
+        const float w = lp == -INFINITY ? 0.f : __expf(lp - m);
+        const float4 o = reinterpret_cast<const float4*>(part_out + p * po)[i];
+        acc.x += w * o.x;
+        acc.y += w * o.y;
+        acc.z += w * o.z;
+        acc.w += w * o.w;
+        den += w;
+      }
+      const float inv = 1.f / den;
+      acc.x *= inv;
+      acc.y *= inv;
+      acc.z *= inv;
+      acc.w *= inv;
+    }
+    if (out_bf16) {
+      ushort4 b;
+      b.x = f32_to_bf16_rne(acc.x);
+      b.y = f32_to_bf16_rne(acc.y);
+      b.z = f32_to_bf16_rne(acc.z);
+      b.w = f32_to_bf16_rne(acc.w);
+      reinterpret_cast<ushort4*>(out)[i] = b;
+    } else {
+      reinterpret_cast<float4*>(out)[i] = acc;
+    }
+    if (c4 == 0) lse[li] = m == -INFINITY ? -INFINITY : m + __logf(den);
+  }
+}
+
 unsigned grid_for(int64_t work, int64_t per_block, unsigned cap) {
   int64_t g = (work + per_block - 1) / per_block;
   if (g < 1) g = 1;
@@ -209,6 +261,20 @@ hipError_t launch_cast_f32_bf16(const float* src, void* dst, int64_t n, hipStrea
   if (n4 <= 0) return hipSuccess;
   hipLaunchKernelGGL(cast_kernel, dim3(grid_for(n4, NT, 8192u)), dim3(NT), 0, st,
                      reinterpret_cast<const float4*>(src), reinterpret_cast<ushort4*>(dst), n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_combine(const float* part_out, const float* part_lse, int split,
+                                int64_t part_out_stride, int64_t part_lse_stride, void* out,
+                                ra_dtype out_dtype, float* lse, int32_t total_t, int32_t h,
+                                int32_t dv, hipStream_t st) {
+  const int64_t n = (int64_t)total_t * h * (dv / 4);
+  if (n <= 0) return hipSuccess;
+  if (split < 1 || (dv % 4) || part_out_stride < n * 4 || part_lse_stride < (int64_t)total_t * h)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(split_combine_kernel, dim3(grid_for(n, NT, 8192u)), dim3(NT), 0, st,
+                     part_out, part_lse, split, part_out_stride, part_lse_stride, out,
+                     out_dtype == RA_BF16 ? 1 : 0, lse, total_t, h, dv / 4, n);
   return hipGetLastError();
 }
 

@@ -54,6 +54,11 @@ struct RankKV {
   const void* k[kMaxCp];
   const void* v[kMaxCp];
   int32_t cp, rank;
+  // KV split of a rank share (4-wave kernel): part p of `split` walks the
+  // blocks p, p + split, ... and writes its float32 partial (out, lse) at
+  // out + p * part_out_stride, lse + p * part_lse_stride (elements)
+  int32_t split;
+  int64_t part_out_stride, part_lse_stride;
 };
 
 // Segment part [lo, hi) after applying a zig-zag half selector.
@@ -92,6 +97,13 @@ hipError_t launch_lse_merge(float* out_acc, float* lse_acc, const float* out_par
                             int32_t n_seq, const int32_t* cu, int32_t part, int32_t max_rows,
                             hipStream_t st);
 hipError_t launch_cast_f32_bf16(const float* src, void* dst, int64_t n, hipStream_t st);
+// out/lse of a row-head = lse-weighted sum of `split` float32 partials
+// (part p at part_out + p * part_out_stride, part_lse + p * part_lse_stride,
+// elements); out has out_dtype.
+hipError_t launch_split_combine(const float* part_out, const float* part_lse, int split,
+                                int64_t part_out_stride, int64_t part_lse_stride, void* out,
+                                ra_dtype out_dtype, float* lse, int32_t total_t, int32_t h,
+                                int32_t dv, hipStream_t st);
 hipError_t launch_zigzag_copy(const void* src, void* dst, int64_t row_bytes, int32_t n_seq,
                               const int32_t* cu_local, const int32_t* src_start,
                               int32_t max_half, bool gather, hipStream_t st);

@@ -194,10 +194,19 @@ ra_status ra_cast_f32_bf16(const float* src, void* dst, int64_t n, void* stream)
  * 2 (bf16): the whole share in one launch, every owner's block walked in
  * ring order with the online-softmax state kept in registers and the final
  * output written by the epilogue (the pass-KV form of the oh-bug page with
- * all blocks resident; no workspace).  fp32 falls back to 1.
+ * all blocks resident; no workspace).  A share too small to give every CU
+ * a workgroup (fewer than 256 of 128 rows x one query head, 4-wave kernel)
+ * is split instead: its blocks are dealt round-robin over up to cp_size
+ * parts, each part's workgroups write a float32 partial (out, lse) into the
+ * workspace, and a combine launch weights the parts by their lse in part
+ * order (deterministic).  The workspace is then parts x (out + lse);
+ * ra_rank_forward_workspace reports it (0 without a split).  The
+ * environment variable RA_FWD_KV_SPLIT=<n> forces n parts (1 = none).
+ * fp32 falls back to 1.
  * events (optional): host array of 2*cp_size hipEvent_t, recorded on the
  * stream right before / after step s's attention launch (with
- * fuse_merge = 2 only events[0], events[1], around the single launch).
+ * fuse_merge = 2 only events[0], events[1], around the launch and its
+ * combine).
  */
 typedef struct ra_rank_desc {
   ra_attn_desc local;

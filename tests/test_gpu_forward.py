@@ -360,6 +360,23 @@ def _full_parity(w, fuse_modes=(0, 1, 2), determinism=False):
     return prob
 
 
+@pytest.mark.parametrize("split", ["1", "3", "8"])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_fused_rank_share_kv_split(split, out_dtype, monkeypatch):
+    """A fused rank share whose blocks are dealt over `split` parts (each a
+    float32 partial), combined by lse weight; 3 parts of 8 blocks are uneven."""
+    monkeypatch.setenv("RA_FWD_KV_SPLIT", split)
+    w = synth.reduced("gqa_32k", 4096, 8)
+    prob, (q, k, v, _) = make_problem(w)
+    ro, rl = oracle.full_attention(to_np(q), to_np(k), to_np(v), w.cu_global())
+    outs, lses = _run_all_ranks(prob, out_dtype, 2)
+    dt = "bf16"
+    for r in range(w.cp):
+        rows = prob.rows(r)
+        check_out(outs[r], ro[rows], dt, f"rank{r} split {split}")
+        check_lse(lses[r], rl[:, rows], f"rank{r} split {split}")
+
+
 def test_mha_8k_workload_full_parity():
     _full_parity(synth.WORKLOADS["mha_8k"], determinism=True)
 
