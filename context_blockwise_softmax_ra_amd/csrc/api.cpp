@@ -552,21 +552,22 @@ ra_status ra_cast_f32_bf16(const float* src, void* dst, int64_t n, void* stream)
 }
 
 // KV split of a fused rank share: a launch of the 4-wave kernel with fewer
-// than 256 workgroups (a rank share of few rows and heads) leaves CUs idle,
-// so its blocks are dealt round-robin over `split` parts (more workgroups),
-// each writing a float32 partial, and a combine kernel weights the parts by
-// their lse.  RA_FWD_KV_SPLIT=<n> in the environment forces n parts (1 =
-// none).
+// than 256 workgroups (a rank share of few rows and heads, or a Ulysses
+// share of few heads) leaves CUs idle, so the share's key tiles are dealt
+// round-robin over `split` parts (more workgroups), each writing a float32
+// partial, and a combine kernel weights the parts by their lse.
+// RA_FWD_KV_SPLIT=<n> in the environment forces n parts (1 = none).
+constexpr int kMaxFwdSplit = 16;
 static int fwd_kv_split(const ra_rank_desc* d, const Checked& c) {
   const ra_attn_desc& L = d->local;
-  if (d->fuse_merge != 2 || L.dtype != RA_BF16 || d->cp_size <= 1) return 1;
+  if (d->fuse_merge != 2 || L.dtype != RA_BF16) return 1;
   if (use_pingpong(&L, RA_PART_ALL)) return 1;
   const char* e = std::getenv("RA_FWD_KV_SPLIT");
-  if (e && *e) return std::max(1, std::min(std::atoi(e), (int)d->cp_size));
+  if (e && *e) return std::max(1, std::min(std::atoi(e), kMaxFwdSplit));
   const long long wg = (long long)L.n_seq * L.hkv * (L.hq / L.hkv) *
                        ((c.max_q_part + ra::kFwdBlockM - 1) / ra::kFwdBlockM);
   if (wg <= 0 || wg >= 256) return 1;
-  return (int)std::min<long long>(d->cp_size, (512 + wg - 1) / wg);
+  return (int)std::min<long long>(8, (512 + wg - 1) / wg);
 }
 
 ra_status ra_rank_forward_workspace(const ra_rank_desc* d, size_t* bytes) {

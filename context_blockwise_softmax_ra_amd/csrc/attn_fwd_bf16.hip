@@ -125,18 +125,18 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
   const int my_row = wq0 + l32;
   const int my_row_rel = my_row - q_lo;
   const int64_t ks_bytes = a.k_stride * 2, vs_bytes = a.v_stride * 2;
-  // blocks of this workgroup: a rank share's blocks kv_part, kv_part +
-  // split, ... (all of them without a split), or the one block
+  // a rank share's blocks (ring steps), or the one block; with a KV split
+  // this workgroup takes every split-th key tile of the share's tile
+  // sequence, starting at tile kv_part
   const int kv_split = MODE == 2 ? max(rk.split, 1) : 1;
-  const int nblocks = MODE == 2 ? (rk.cp - kv_part + kv_split - 1) / kv_split : 1;
+  const int nblocks = MODE == 2 ? rk.cp : 1;
 
-  // block li of this workgroup, with the number of key tiles it visits
-  auto get_block = [&](int li) -> Block {
+  // block bi of this workgroup, with the number of key tiles it visits
+  auto get_block = [&](int bi) -> Block {
     Block blk;
     const void* kp;
     const void* vp;
     int kpart;
-    const int bi = kv_part + li * kv_split;  // ring step of the block
     if (MODE == 2) {
       const int owner = (rk.rank - bi + rk.cp) % rk.cp;
       kp = rk.k[owner];
@@ -188,20 +188,26 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
       c.blk = get_block(c.bi);
     } while (c.blk.ntiles == 0);
   };
-  int total = 0;
-  for (int bi = 0; bi < nblocks; ++bi) total += get_block(bi).ntiles;
+  // the part's next tile: split tiles on
+  auto advance_part = [&](Cursor& c) {
+    for (int i = 0; i < kv_split; ++i) advance(c);
+  };
+  int total_all = 0;
+  for (int bi = 0; bi < nblocks; ++bi) total_all += get_block(bi).ntiles;
+  const int total = total_all > kv_part ? (total_all - kv_part + kv_split - 1) / kv_split : 0;
   if (total == 0 && MERGE) return;  // merging an empty block is the identity
 
   TileLoader<DQK, DV, NW> ld;
   ld.init(ks_bytes, vs_bytes, wave, lane);
   Cursor lc, cc;
   first(lc);
+  for (int i = 0; i < kv_part; ++i) advance(lc);
   cc = lc;
   auto issue_next = [&](char* stage) {
     ld.issue_k(lc.blk.kb + (int64_t)lc.t * BN * ks_bytes, ks_bytes, lc.blk.klen - lc.t * BN, stage);
     ld.issue_v(lc.blk.vb + (int64_t)lc.t * BN * vs_bytes, vs_bytes, lc.blk.klen - lc.t * BN,
                stage + G::K_BYTES);
-    advance(lc);
+    advance_part(lc);
   };
   // the first K/V tile streams in while Q is fetched
   if (total > 0) issue_next(smem0);
@@ -328,7 +334,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
         }
       }
     }
-    advance(cc);
+    advance_part(cc);
     // next tile landed (own loads) and every wave is done with this one
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();

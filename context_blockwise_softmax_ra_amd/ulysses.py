@@ -50,17 +50,21 @@ class UlyssesProblem:
                            self.cu, causal=causal, scale=self.scale)
 
     def alloc_forward(self, out_dtype=torch.bfloat16):
+        """(out, lse, workspace) of one rank; the workspace holds the float32
+        partials of a KV-split share (None when the library splits nothing)."""
         dev = self.q[0].device
         out = torch.empty((self.T, self.hs, self.dv), dtype=out_dtype, device=dev)
         lse = torch.empty((self.hs, self.T), dtype=torch.float32, device=dev)
-        return out, lse
+        n = L.ra_rank_forward_workspace(self.forward_desc(0, out, lse))
+        ws = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
+        return out, lse, ws
 
-    def forward_desc(self, r: int, out, lse, events=None) -> L.RankDesc:
-        return L.rank_desc(self.local_desc(r), 1, 0, [self.k[r]], [self.v[r]], out, lse, None,
-                           2, events)
+    def forward_desc(self, r: int, out, lse, workspace=None, events=None) -> L.RankDesc:
+        return L.rank_desc(self.local_desc(r), 1, 0, [self.k[r]], [self.v[r]], out, lse,
+                           workspace, 2, events)
 
-    def forward(self, r: int, out, lse, events=None, stream=None):
-        L.ra_rank_forward(self.forward_desc(r, out, lse, events), stream)
+    def forward(self, r: int, out, lse, workspace=None, events=None, stream=None):
+        L.ra_rank_forward(self.forward_desc(r, out, lse, workspace, events), stream)
 
     def work(self, r: int):
         """(visible pairs x heads, tiles visited, tiles skipped) of rank r's share."""

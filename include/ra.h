@@ -196,12 +196,13 @@ ra_status ra_cast_f32_bf16(const float* src, void* dst, int64_t n, void* stream)
  * output written by the epilogue (the pass-KV form of the oh-bug page with
  * all blocks resident; no workspace).  A share too small to give every CU
  * a workgroup (fewer than 256 of 128 rows x one query head, 4-wave kernel)
- * is split instead: its blocks are dealt round-robin over up to cp_size
- * parts, each part's workgroups write a float32 partial (out, lse) into the
- * workspace, and a combine launch weights the parts by their lse in part
- * order (deterministic).  The workspace is then parts x (out + lse);
+ * is split instead: its key tiles (over all blocks, in ring order) are
+ * dealt round-robin over up to 8 parts, each part's workgroups write a
+ * float32 partial (out, lse) into the workspace, and a combine launch
+ * weights the parts by their lse in part order (deterministic).  The workspace is then parts x (out + lse);
  * ra_rank_forward_workspace reports it (0 without a split).  The
- * environment variable RA_FWD_KV_SPLIT=<n> forces n parts (1 = none).
+ * environment variable RA_FWD_KV_SPLIT=<n> forces n parts (1 = none, at
+ * most 16).
  * fp32 falls back to 1.
  * events (optional): host array of 2*cp_size hipEvent_t, recorded on the
  * stream right before / after step s's attention launch (with

@@ -36,8 +36,8 @@ def _run(prob, r, kernel=None):
     if kernel:
         os.environ["RA_FWD_KERNEL"] = kernel
     try:
-        out, lse = prob.alloc_forward()
-        prob.forward(r, out, lse)
+        out, lse, ws = prob.alloc_forward()
+        prob.forward(r, out, lse, ws)
         torch.cuda.synchronize()
     finally:
         if old is None:
