@@ -53,12 +53,6 @@ constexpr int BM = kFwdBlockM;
 constexpr int NW = kFwdWaves;
 constexpr int NT = NW * 64;
 
-// Rescale threshold (log2 units): the running max used for the exponent is
-// only raised when a row's max grows by more than this, so the output
-// rescale is skipped on most tiles.  Exact: numerator, row sum and lse all
-// use the same (possibly stale) max; p stays <= 2^8.
-constexpr float kRescaleLog2 = 8.0f;
-
 // MODE: 0 = one non-causal block, 1 = one causal block (both as described by
 // the AttnArgs parts), 2 = a rank's whole share: the C blocks of RankKV in
 // ring order, merged in registers (no partials, no separate merge), 3 = a
@@ -291,41 +285,12 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
           }
       }
       // ---- online softmax (log2 domain, lazily rescaled)
-      float mx = max3f(s[0][0], s[0][1], s[0][2]);
-#pragma unroll
-      for (int i = 3; i < 15; i += 2) mx = max3f(mx, s[0][i], s[0][i + 1]);
-      mx = max3f(mx, s[0][15], s[1][0]);
-#pragma unroll
-      for (int i = 1; i < 15; i += 2) mx = max3f(mx, s[1][i], s[1][i + 1]);
-      mx = fmaxf(mx, s[1][15]);
-      mx = xhalf_max(mx);
-      const bool raise = (mx - m_run) * c2 > kRescaleLog2;  // true on the first live tile
-      if (__builtin_amdgcn_ballot_w64(raise)) {
-        const float m_new = raise ? mx : m_run;
-        const float m_use_new = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_use_new) * c2);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int tt = 0; tt < G::OT; ++tt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[tt][i] *= alpha;
-      }
-      const float mc = ((m_run == -INFINITY) ? 0.f : m_run) * c2;
-      float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[hh][i], c2, -mc));
-          if (i & 1) rs1 += p; else rs0 += p;
-          s[hh][i] = p;
-        }
-      l_run += rs0 + rs1;
+      bf16x8 pk[4];
+      online_softmax_tile(s[0], s[1], c2, m_run, l_run, o, pk);
       // ---- O^T += V^T * P^T : 4 k-steps of 16 keys
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
-        const bf16x8 pb = pack8(s[bb >> 1], 8 * (bb & 1));
+        const bf16x8 pb = pk[bb];
 #pragma unroll
         for (int tt = 0; tt < G::OT; ++tt) {
           const char* vp = vsm + bb * 16 * G::VROWB;

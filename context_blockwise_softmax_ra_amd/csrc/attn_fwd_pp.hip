@@ -50,11 +50,6 @@ constexpr int PW = 8;                        // waves per workgroup
 constexpr int PT = PW * 64;                  // threads per workgroup
 constexpr int PBM = PW * kFwdRowsPerWave;    // 256 query rows per workgroup
 
-// Rescale threshold (log2 units), as in the 4-wave kernel: the running max
-// is only raised when a row's max grows by more than this; numerator, row
-// sum and lse use the same (possibly stale) max, so the result is exact.
-constexpr float kRescaleLog2 = 8.0f;
-
 // How many matrix-core products the LDS operand reads run ahead of, in the
 // S = K Q^T and the P*V blocks (latency cover without the register cost of
 // reading a whole tile at once).
@@ -349,39 +344,7 @@ __global__ __launch_bounds__(PT, 1) void attn_fwd_pp_kernel(AttnArgs a, RankKV r
           if (!ok) s[hh][i] = -INFINITY;
         }
     }
-    float mx = max3f(s[0][0], s[0][1], s[0][2]);
-#pragma unroll
-    for (int i = 3; i < 15; i += 2) mx = max3f(mx, s[0][i], s[0][i + 1]);
-    mx = max3f(mx, s[0][15], s[1][0]);
-#pragma unroll
-    for (int i = 1; i < 15; i += 2) mx = max3f(mx, s[1][i], s[1][i + 1]);
-    mx = fmaxf(mx, s[1][15]);
-    mx = xhalf_max(mx);
-    const bool raise = (mx - m_run) * c2 > kRescaleLog2;
-    if (__builtin_amdgcn_ballot_w64(raise)) {
-      const float m_new = raise ? mx : m_run;
-      const float m_use_new = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_use_new) * c2);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int tt = 0; tt < G::OT; ++tt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[tt][i] *= alpha;
-    }
-    const float mc = ((m_run == -INFINITY) ? 0.f : m_run) * c2;
-    float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(s[hh][i], c2, -mc));
-        if (i & 1) rs1 += pv; else rs0 += pv;
-        s[hh][i] = pv;
-      }
-    l_run += rs0 + rs1;
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb) p[bb] = pack8(s[bb >> 1], 8 * (bb & 1));
+    online_softmax_tile(s[0], s[1], c2, m_run, l_run, o, p);
   };
 
   // One tile step st (two phases).  K(st) is in kcur, V(st-1) in vprev.

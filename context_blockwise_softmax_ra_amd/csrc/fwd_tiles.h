@@ -112,8 +112,87 @@ struct TileLoader {
   }
 };
 
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  return __builtin_fmaxf(a, __builtin_fmaxf(b, c));
+// In-lane maximum of the 32 scores a lane holds of a 64-key S tile (the
+// lane's query row, one half of the keys), as two left-folded fmaxf chains:
+// the backend fuses those into v_max3_f32 (two scores per instruction),
+// while a chain of three-way maxima gets re-associated into pairwise
+// v_max_f32 (three instructions per four scores).  The softmax shares its
+// SIMD's vector issue with the matrix-core products of the other wave
+// there, so the instruction count matters.
+__device__ __forceinline__ float lane_max32(const mfma::f32x16& s0, const mfma::f32x16& s1) {
+  float a = __builtin_fmaxf(s0[0], s0[1]);
+  float b = __builtin_fmaxf(s1[0], s1[1]);
+#pragma unroll
+  for (int i = 2; i < 16; ++i) {
+    a = __builtin_fmaxf(a, s0[i]);
+    b = __builtin_fmaxf(b, s1[i]);
+  }
+  return __builtin_fmaxf(a, b);
+}
+
+// P operand of a lane's 32 scores against the offset mc (the running max
+// times c2): p = 2^(c2 * s - mc), rounded to bf16 into p[4] (key order of
+// the P^T operand: entries 8bb..8bb+7 of the pair (s0, s1) make p[bb]).
+// Returns the float32 sum of the unrounded values; s is left intact.
+__device__ __forceinline__ float exp2_pack_sum(const mfma::f32x16& s0, const mfma::f32x16& s1,
+                                               float c2, float mc, mfma::bf16x8 (&p)[4]) {
+  float a = 0.f, b = 0.f;
+  mfma::u32x4 w[4];
+#pragma unroll
+  for (int i = 0; i < 32; i += 2) {
+    const float x0 = __builtin_amdgcn_exp2f(fmaf(i < 16 ? s0[i & 15] : s1[i & 15], c2, -mc));
+    const float x1 = __builtin_amdgcn_exp2f(fmaf(i < 16 ? s0[(i & 15) + 1] : s1[(i & 15) + 1], c2, -mc));
+    a = i == 0 ? x0 : a + x0;
+    b = i == 0 ? x1 : b + x1;
+    w[i >> 3][(i >> 1) & 3] = mfma::pack_bf16x2(x0, x1);
+  }
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) p[bb] = mfma::as_bf16x8(w[bb]);
+  return a + b;
+}
+
+// Online softmax of one 64-key S tile for the lane's query row (log2
+// domain; scores s, c2 = softmax scale * log2(e)).  The running max m_run
+// is raised lazily: only when a score exceeds it by more than 2^8 in
+// probability.  The numerator, the row sum l_run and the lse all use the
+// same (possibly stale) max, so the result is exact.
+//
+// The probabilities are first taken against the running max.  A lane whose
+// 32 of them sum to at most 2^8 has none above 2^8, so no raise is due for
+// it; only when some lane exceeds that (or has no finite max yet, as on a
+// row's first tile) are the row maximum and the raise worked out, and P
+// recomputed if the max moved.  This keeps the row-max reduction out of
+// the common tile and reaches the same state as testing the max first.
+template <int OT>
+__device__ __forceinline__ void online_softmax_tile(const mfma::f32x16& s0, const mfma::f32x16& s1,
+                                                    float c2, float& m_run, float& l_run,
+                                                    mfma::f32x16 (&o)[OT], mfma::bf16x8 (&p)[4]) {
+  constexpr float kRescaleLog2 = 8.0f;
+  constexpr float kSumBound = 256.0f;  // 2^kRescaleLog2
+  const bool all_finite = !__builtin_amdgcn_ballot_w64(m_run == -INFINITY);
+  float ts = 0.f;
+  if (all_finite) ts = exp2_pack_sum(s0, s1, c2, m_run * c2, p);
+  if (!all_finite || __builtin_amdgcn_ballot_w64(!(ts <= kSumBound))) {
+    const float mx = mfma::xhalf_max(lane_max32(s0, s1));
+    const bool raise = (mx - m_run) * c2 > kRescaleLog2;  // true on a row's first live tile
+    const bool any_raise = __builtin_amdgcn_ballot_w64(raise) != 0;
+    if (any_raise) {
+      const float m_new = raise ? mx : m_run;
+      const float m_use_new = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_use_new) * c2);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int tt = 0; tt < OT; ++tt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[tt][i] *= alpha;
+    }
+    if (any_raise || !all_finite) {
+      const float mc = ((m_run == -INFINITY) ? 0.f : m_run) * c2;
+      ts = exp2_pack_sum(s0, s1, c2, mc, p);
+    }
+  }
+  l_run += ts;
 }
 
 // How a KV block meets the rows of a workgroup.
