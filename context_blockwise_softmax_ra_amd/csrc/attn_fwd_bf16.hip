@@ -274,15 +274,12 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
       // ---- mask (tiles crossing the causal diagonal, a part end, or the
       // segment's half for second-half-only blocks)
       if (need_mask) {
-        const bool row_ok = kind != KIND_LATE_ROWS || my_row_rel >= qhalf;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kr = kt0 + 32 * hh + ((i >> 3) << 4) + (g << 3) + (i & 7);
-            const bool ok = row_ok && (kr < klen) && (kind != KIND_CAUSAL || kr <= my_row_rel + diag);
-            if (!ok) s[hh][i] = -INFINITY;
-          }
+        // last visible key of the row, relative to the lane's first key
+        const int base = kt0 + (g << 3);
+        int lim = klen - 1 - base;
+        if (kind == KIND_CAUSAL) lim = min(lim, my_row_rel + diag - base);
+        if (kind == KIND_LATE_ROWS && my_row_rel < qhalf) lim = -1;
+        mask_scores(s[0], s[1], lim);
       }
       // ---- online softmax (log2 domain, lazily rescaled)
       bf16x8 pk[4];

@@ -334,15 +334,12 @@ __global__ __launch_bounds__(PT, 1) void attn_fwd_pp_kernel(AttnArgs a, RankKV r
     p_live = s_live;
     if (!s_live) return;
     if (s_mask) {
-      const bool row_ok = s_kind != KIND_LATE_ROWS || my_row_rel >= qhalf;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kr = s_kt0 + 32 * hh + ((i >> 3) << 4) + (g << 3) + (i & 7);
-          const bool ok = row_ok && (kr < s_klen) && (s_kind != KIND_CAUSAL || kr <= my_row_rel);
-          if (!ok) s[hh][i] = -INFINITY;
-        }
+      // last visible key of the row, relative to the lane's first key
+      const int base = s_kt0 + (g << 3);
+      int lim = s_klen - 1 - base;
+      if (s_kind == KIND_CAUSAL) lim = min(lim, my_row_rel - base);
+      if (s_kind == KIND_LATE_ROWS && my_row_rel < qhalf) lim = -1;
+      mask_scores(s[0], s[1], lim);
     }
     online_softmax_tile(s[0], s[1], c2, m_run, l_run, o, p);
   };

@@ -112,6 +112,20 @@ struct TileLoader {
   }
 };
 
+// Masks the 32 scores of a lane in a 64-key S tile: entry i of C tile hh is
+// key offset e = 32*hh + 16*(i/8) + (i%8) past the lane's first key (the
+// tile's first key plus 8*(lane/32)), and is kept iff e <= lim.  The caller
+// folds every masking rule of the lane's row into the one limit, so each
+// score costs a compare against an inline constant and a select.
+__device__ __forceinline__ void mask_scores(mfma::f32x16& s0, mfma::f32x16& s1, int lim) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = ((i >> 3) << 4) + (i & 7);
+    s0[i] = e <= lim ? s0[i] : -INFINITY;
+    s1[i] = e + 32 <= lim ? s1[i] : -INFINITY;
+  }
+}
+
 // In-lane maximum of the 32 scores a lane holds of a 64-key S tile (the
 // lane's query row, one half of the keys), as two left-folded fmaxf chains:
 // the backend fuses those into v_max3_f32 (two scores per instruction),
