@@ -181,6 +181,49 @@ def test_softmax_scale_override(scale, kernel, monkeypatch):
         check_lse(lse, rl, f"scale {scale} causal {causal}")
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("dims", [(128, 128), (192, 128)])
+@pytest.mark.parametrize("pattern", ["rising", "falling", "late_jump"])
+def test_running_max_paths(pattern, dims, kernel, monkeypatch):
+    """Scores shaped so that the kernels' online softmax takes each of its
+    paths on purpose: "rising" raises the running max on every 64-key tile
+    (about 19 log2 units per tile, so the tile sum passes 2^8 and the row max
+    and rescale run each time); "falling" leaves every later tile far under
+    the first key (probabilities underflow to zero against the running max);
+    "late_jump" keeps N(0,1)-sized scores and gives one key per segment a
+    score some 60 log2 units above the rest."""
+    monkeypatch.setenv("RA_FWD_KERNEL", kernel)
+    dqk, dv = dims
+    lq = [333, 130, 200]
+    cu = _cu(lq)
+    T, hq, hkv = int(cu[-1]), 4, 2
+    g = torch.Generator().manual_seed(zlib.crc32(f"{pattern}{dims}".encode()) & 0xFFFF)
+    q = 0.3 * torch.randn(T, hq, dqk, generator=g)
+    k = 0.3 * torch.randn(T, hkv, dqk, generator=g)
+    v = torch.randn(T, hkv, dv, generator=g)
+    pos = torch.cat([torch.arange(n, dtype=torch.float32) for n in lq])  # key index in segment
+    scale = dqk ** -0.5
+    slope = 0.3 / (scale * 1.4426950408889634)  # 0.3 log2 units per key
+    q[:, :, 0] = 1.0
+    if pattern == "rising":
+        k[:, :, 0] = (slope * pos)[:, None]
+    elif pattern == "falling":
+        k[:, :, 0] = (-2.0 * slope * pos)[:, None]
+    else:
+        jump = torch.zeros(T)
+        for a, n in zip(cu[:-1], lq):
+            jump[int(a) + (2 * n) // 3] = 60.0 / (scale * 1.4426950408889634)
+        k[:, :, 0] = jump[:, None]
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    for causal in (True, False):
+        tag = f"{pattern} dims {dims} kernel {kernel} causal {causal}"
+        log(tag)
+        out, lse = run_block(q, k, v, cu, cu, 0, 0, causal)
+        ro, rl, cov = block_ref(to_np(q), to_np(k), to_np(v), cu, cu, 0, 0, causal)
+        check_out(out, ro, "bf16", tag)
+        check_lse(lse, rl, tag)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_all_empty_segments_are_a_no_op(dtype, monkeypatch):
     """Segments that are all empty (the degenerate batch): every call succeeds
