@@ -745,9 +745,31 @@ static bool bwd_kv_split(const ra_attn_desc* d, const ra::AttnArgs& a) {
   return (long long)a.n_seq * a.hkv * a.n_ktiles < 256;
 }
 
+// dK/dV query split of a rank-backward step (the workspace holds the
+// partials): workgroups of 128 keys, shared by up to kMaxQsplit workgroups
+// that each take a contiguous share of the key tile's query iterations.
+// Split until the launch has 256 workgroups (one per CU), and at least in
+// two on a causal block, whose first key tiles see every query and the last
+// ones only a few.  RA_BWD_QSPLIT=n in the environment forces n.
+constexpr int kMaxQsplit = 4;
+static int bwd_qsplit(const ra_attn_desc* d, const Checked& c) {
+  const char* e = std::getenv("RA_BWD_QSPLIT");
+  if (e && *e) return std::max(1, std::min(std::atoi(e), kMaxQsplit));
+  const long long wg = (long long)d->n_seq * d->hkv * ((c.max_k_part + 127) / 128);
+  int n = 1;
+  while (n < kMaxQsplit && wg * n < 256) n *= 2;
+  if (d->causal && n < 2) n = 2;
+  return n;
+}
+
+// Bytes of one query share's dK/dV partial: every key row of the block.
+static size_t bwd_part_bytes(const ra_attn_desc* d, const Checked& c) {
+  return align256((size_t)c.total_k * d->hkv * (d->dqk + d->dv) * sizeof(float));
+}
+
 static ra_status launch_bwd(const ra_attn_desc* d, const Checked& c, const void* dout,
                             const float* lse, const float* delta, float* dq, float* dk, float* dv,
-                            hipStream_t st) {
+                            hipStream_t st, int qsplit = 1, float* part = nullptr) {
   ra::AttnArgs a = make_args(d, c);
   a.n_ktiles = (c.max_k_part + 127) / 128;  // 128-key tiles of the dK/dV kernel
   a.dout = dout;
@@ -756,8 +778,14 @@ static ra_status launch_bwd(const ra_attn_desc* d, const Checked& c, const void*
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
+  a.qsplit = part ? qsplit : 1;
+  a.part_keys = c.total_k;
+  a.dk_part = part;
+  a.dv_part = part ? part + (size_t)(qsplit - 1) * c.total_k * d->hkv * d->dqk : nullptr;
+  // the query-split-over-waves form only where no workspace split runs
+  const bool kv_split = a.qsplit == 1 && bwd_kv_split(d, a);
   hipError_t e =
-      ra::launch_attn_bwd_bf16(a, d->dqk, d->dv, d->causal != 0, bwd_kv_split(d, a), st);
+      ra::launch_attn_bwd_bf16(a, d->dqk, d->dv, d->causal != 0, kv_split, c.total_k, st);
   if (e == hipErrorInvalidValue) return fail(RA_ERR_UNSUPPORTED, "backward variant not built");
   if (e != hipSuccess) return hip_fail(e, "attention backward launch");
   return RA_OK;
@@ -793,12 +821,47 @@ ra_status ra_block_attn_bwd(const ra_attn_desc* d, const void* dout, const float
   return st == RA_OK ? ok() : st;
 }
 
+// Step s of a rank backward as a block descriptor (plan of the ring step).
+static ra_status rank_bwd_step(const ra_rank_bwd_desc* d, int s, ra_attn_desc* sd, Checked* cs,
+                               int* owner) {
+  const Step p = plan_step(d->rank, s, d->cp_size);
+  *sd = d->local;
+  sd->k = d->k_blocks[p.owner];
+  sd->v = d->v_blocks[p.owner];
+  sd->causal = p.causal;
+  sd->q_part = p.q_part;
+  sd->k_part = p.k_part;
+  *owner = p.owner;
+  return check_desc(sd, true, cs);
+}
+
+// Workspace: delta [hq, total_q], then the dK/dV partials of query shares
+// 1 .. qsplit-1 of the step kind that splits most.  Every kind a rank of
+// the ring can meet is counted (the diagonal block, an earlier and a later
+// owner's block), so one workspace serves every rank.
 ra_status ra_rank_backward_workspace(const ra_rank_bwd_desc* d, size_t* bytes) {
   if (!d || !bytes) return fail(RA_ERR_INVALID_ARG, "NULL argument");
   Checked c;
   ra_status st = check_rank_common(d->local, d->cp_size, d->rank, d->k_blocks, d->v_blocks, &c);
   if (st != RA_OK) return st;
-  *bytes = align256((size_t)c.total_q * d->local.hq * sizeof(float));
+  size_t parts = 0;
+  const int n_kinds = d->cp_size > 1 ? 3 : 1;
+  for (int kind = 0; kind < n_kinds; ++kind) {
+    // the plan of rank 0 (s = 0), of the last rank at s = 1 (owner before
+    // it) and of rank 0 at s = 1 (owner after it)
+    const Step p = kind == 0 ? plan_step(0, 0, d->cp_size)
+                             : plan_step(kind == 1 ? d->cp_size - 1 : 0, 1, d->cp_size);
+    ra_attn_desc sd = d->local;
+    sd.k = d->k_blocks[0];
+    sd.v = d->v_blocks[0];
+    sd.causal = p.causal;
+    sd.q_part = p.q_part;
+    sd.k_part = p.k_part;
+    Checked cs;
+    if ((st = check_desc(&sd, true, &cs)) != RA_OK) return st;
+    parts = std::max(parts, (size_t)(bwd_qsplit(&sd, cs) - 1) * bwd_part_bytes(&sd, cs));
+  }
+  *bytes = align256((size_t)c.total_q * d->local.hq * sizeof(float)) + parts;
   return ok();
 }
 
@@ -830,24 +893,25 @@ ra_status ra_rank_backward(const ra_rank_bwd_desc* d, void* stream) {
       return st;
   }
   float* delta = static_cast<float*>(d->workspace);
+  const size_t delta_b = align256((size_t)c.total_q * L.hq * sizeof(float));
+  float* part = reinterpret_cast<float*>(static_cast<char*>(d->workspace) + delta_b);
   hipError_t e = ra::launch_bwd_delta(d->out, d->out_dtype, d->dout, L.dtype, c.total_q, L.hq,
                                       L.dv, delta, hs);
   if (e != hipSuccess) return hip_fail(e, "delta launch");
   for (int s = 0; s < d->cp_size; ++s) {
-    const Step p = plan_step(d->rank, s, d->cp_size);
-    ra_attn_desc sd = L;
-    sd.k = d->k_blocks[p.owner];
-    sd.v = d->v_blocks[p.owner];
-    sd.causal = p.causal;
-    sd.q_part = p.q_part;
-    sd.k_part = p.k_part;
+    ra_attn_desc sd;
     Checked cs;
-    if ((st = check_desc(&sd, true, &cs)) != RA_OK) return st;
+    int owner;
+    if ((st = rank_bwd_step(d, s, &sd, &cs, &owner)) != RA_OK) return st;
+    // the partials fit the workspace (sized by ra_rank_backward_workspace)
+    const int qsplit = bwd_qsplit(&sd, cs);
+    if ((size_t)(qsplit - 1) * bwd_part_bytes(&sd, cs) > d->workspace_bytes - delta_b)
+      return fail(RA_ERR_INVALID_ARG, "workspace too small for the dK/dV query split");
     if (d->events && d->events[2 * s] &&
         (e = hipEventRecord((hipEvent_t)d->events[2 * s], hs)) != hipSuccess)
       return hip_fail(e, "event record");
-    st = launch_bwd(&sd, cs, d->dout, d->lse, delta, d->dq, d->dk_blocks[p.owner],
-                    d->dv_blocks[p.owner], hs);
+    st = launch_bwd(&sd, cs, d->dout, d->lse, delta, d->dq, d->dk_blocks[owner],
+                    d->dv_blocks[owner], hs, qsplit, qsplit > 1 ? part : nullptr);
     if (st != RA_OK) return st;
     if (d->events && d->events[2 * s + 1] &&
         (e = hipEventRecord((hipEvent_t)d->events[2 * s + 1], hs)) != hipSuccess)

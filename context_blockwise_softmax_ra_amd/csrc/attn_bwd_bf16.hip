@@ -101,7 +101,10 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
   // V of the workgroup's keys (dual layout): read as B operands of dP
   __shared__ __attribute__((aligned(1024))) char vsm[KBN * G::OROWB];
 
+  const int nsp = QS ? 1 : a.qsplit;  // workgroups sharing a key tile
   int b = xcd_remap(blockIdx.x, gridDim.x);
+  const int sp = b % nsp;
+  b /= nsp;
   const int kt = b % a.n_ktiles;
   b /= a.n_ktiles;
   const int kvh = b % a.hkv;
@@ -146,7 +149,10 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
   const int n_qt = (qlen + KV_BQ - 1) / KV_BQ;
   const int qt_begin = CAUSAL ? (kt * KBN) / KV_BQ : 0;
   const int per_head = n_qt - qt_begin;
-  const int n_it = per_head > 0 ? per_head * a.group : 0;
+  const int n_all = per_head > 0 ? per_head * a.group : 0;
+  // this workgroup's share of the iterations: [it_lo, n_it)
+  const int it_lo = (int)((int64_t)n_all * sp / nsp);
+  const int n_it = (int)((int64_t)n_all * (sp + 1) / nsp);
   const float c2 = a.scale_log2;
   const int arow = sigma(l32);  // A-operand row of this lane (query row in the tile)
   const int trr = tr_row(lane), trc = tr_col_bytes(lane);
@@ -239,7 +245,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
 
   // iterations of this wave: all (it += 1), or with QS every 4th from the
   // wave's index
-  const int it0 = QS ? wave : 0, istep = QS ? NT / 64 : 1;
+  const int it0 = it_lo + (QS ? wave : 0), istep = QS ? NT / 64 : 1;
   if (it0 < n_it) issue(it0, qs0[ws], os0[ws], ld0[ws]);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();  // V (and, without QS, the first tile) in LDS
@@ -309,18 +315,76 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
 
   // C rows = keys 8*(i/4) + 4g + i%4 of the wave, column = dim 32*nt + l32
   const float scale = a.scale;
+  if (sp == 0) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int kr = wk_rel + 8 * (i >> 2) + 4 * g + (i & 3);
-    if (kr >= klen) continue;
-    const int64_t key = k_lo + kr;
-    float* dkp = a.dk + (key * a.hkv + kvh) * DQK + l32;
-    float* dvp = a.dv + (key * a.hkv + kvh) * DV + l32;
+    for (int i = 0; i < 16; ++i) {
+      const int kr = wk_rel + 8 * (i >> 2) + 4 * g + (i & 3);
+      if (kr >= klen) continue;
+      const int64_t key = k_lo + kr;
+      float* dkp = a.dk + (key * a.hkv + kvh) * DQK + l32;
+      float* dvp = a.dv + (key * a.hkv + kvh) * DV + l32;
 #pragma unroll
-    for (int nt = 0; nt < G::NQT; ++nt) dkp[32 * nt] += scale * dk[nt][i];
+      for (int nt = 0; nt < G::NQT; ++nt) dkp[32 * nt] += scale * dk[nt][i];
 #pragma unroll
-    for (int nt = 0; nt < G::NVT; ++nt) dvp[32 * nt] += dv[nt][i];
+      for (int nt = 0; nt < G::NVT; ++nt) dvp[32 * nt] += dv[nt][i];
+    }
+  } else {
+    const int64_t row0 = (int64_t)(sp - 1) * a.part_keys;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kr = wk_rel + 8 * (i >> 2) + 4 * g + (i & 3);
+      if (kr >= klen) continue;
+      const int64_t key = row0 + k_lo + kr;
+      float* dkp = a.dk_part + (key * a.hkv + kvh) * DQK + l32;
+      float* dvp = a.dv_part + (key * a.hkv + kvh) * DV + l32;
+#pragma unroll
+      for (int nt = 0; nt < G::NQT; ++nt) dkp[32 * nt] = scale * dk[nt][i];
+#pragma unroll
+      for (int nt = 0; nt < G::NVT; ++nt) dvp[32 * nt] = dv[nt][i];
+    }
   }
+}
+
+// dk/dv += the stored partials of query shares 1 .. qsplit-1, in share
+// order, for every key the dK/dV launch covered (keys inside the k part of
+// a segment whose q part is not empty).  One thread per 4 floats of a key's
+// [hkv, dqk] + [hkv, dv] gradient rows; HBM-bound.
+__global__ __launch_bounds__(256) void bwd_qsplit_reduce_kernel(AttnArgs a, int dqk, int dv,
+                                                                int total_k) {
+  const int nk4 = a.hkv * dqk / 4, row4 = nk4 + a.hkv * dv / 4;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)total_k * row4) return;
+  const int key = (int)(idx / row4), c = (int)(idx % row4);
+  int lo = 0, hi = a.n_seq;  // segment of the key: cu_k[seg] <= key < cu_k[seg + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.cu_k[mid] <= key) lo = mid; else hi = mid;
+  }
+  int q_lo, q_hi, k_lo, k_hi;
+  part_range(a.cu_q[lo], a.cu_q[lo + 1], a.q_part, &q_lo, &q_hi);
+  part_range(a.cu_k[lo], a.cu_k[lo + 1], a.k_part, &k_lo, &k_hi);
+  if (q_hi <= q_lo || key < k_lo || key >= k_hi) return;
+  float* dst;
+  const float* src;
+  int64_t stride;
+  if (c < nk4) {
+    dst = a.dk + (int64_t)key * a.hkv * dqk + 4 * c;
+    src = a.dk_part + (int64_t)key * a.hkv * dqk + 4 * c;
+    stride = (int64_t)a.part_keys * a.hkv * dqk;
+  } else {
+    dst = a.dv + (int64_t)key * a.hkv * dv + 4 * (c - nk4);
+    src = a.dv_part + (int64_t)key * a.hkv * dv + 4 * (c - nk4);
+    stride = (int64_t)a.part_keys * a.hkv * dv;
+  }
+  float4 acc = *reinterpret_cast<const float4*>(dst);
+  for (int s = 1; s < a.qsplit; ++s) {
+    const float4 x = *reinterpret_cast<const float4*>(src + (s - 1) * stride);
+    acc.x += x.x;
+    acc.y += x.y;
+    acc.z += x.z;
+    acc.w += x.w;
+  }
+  *reinterpret_cast<float4*>(dst) = acc;
 }
 
 // ===========================================================================
@@ -505,14 +569,15 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attn_bwd_bf16(const AttnArgs& a0, int dqk, int dv, bool causal, bool kv_split,
-                                hipStream_t st) {
+                                int total_k, hipStream_t st) {
   // a0.n_qtiles counts 128-row query tiles, a0.n_ktiles 128-key tiles; with
   // kv_split (d_qk = 128 only) the dK/dV kernel runs 32-key workgroups
   AttnArgs a = a0;
   const long long nq = (long long)a.n_seq * a.hkv * a.n_qtiles * a.group;
   AttnArgs ak = a;
   if (kv_split) ak.n_ktiles = 4 * a.n_ktiles;
-  const long long nk = (long long)a.n_seq * a.hkv * ak.n_ktiles;
+  if (kv_split || ak.qsplit < 1) ak.qsplit = 1;
+  const long long nk = (long long)a.n_seq * a.hkv * ak.n_ktiles * ak.qsplit;
   if (nq > 0x7fffffffLL || nk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (kv_split && dqk != 128) return hipErrorInvalidValue;
 #define RA_BWD_LAUNCH(DQ, DVV, C, QSPLIT)                                                      \
@@ -539,6 +604,14 @@ hipError_t launch_attn_bwd_bf16(const AttnArgs& a0, int dqk, int dv, bool causal
     return hipErrorInvalidValue;
   }
 #undef RA_BWD_LAUNCH
+  if (ak.qsplit > 1 && nk > 0) {
+    const long long n4 = (long long)total_k * a.hkv * (dqk + dv) / 4;
+    const long long nb = (n4 + 255) / 256;
+    if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (nb > 0)
+      hipLaunchKernelGGL(bwd_qsplit_reduce_kernel, dim3((unsigned)nb), dim3(256), 0, st, ak, dqk,
+                         dv, total_k);
+  }
   return hipGetLastError();
 }
 

@@ -46,6 +46,15 @@ struct AttnArgs {
   float* dq;              // [total_q, hq, dqk] fp32 accumulate
   float* dk;              // [total_k, hkv, dqk] fp32 accumulate
   float* dv;              // [total_k, hkv, dv] fp32 accumulate
+  // dK/dV query split: qsplit workgroups share each key tile, each taking a
+  // contiguous share of its (query head, query tile) iterations.  Share 0
+  // adds into dk/dv; share s > 0 stores its scaled partial at dk_part /
+  // dv_part + (s - 1) * part_keys rows (same row layout as dk/dv), which
+  // bwd_qsplit_reduce then adds in share order.
+  int32_t qsplit;
+  int32_t part_keys;
+  float* dk_part;
+  float* dv_part;
 };
 
 // KV blocks of every owner for a rank's fused forward (one launch per rank).
@@ -111,6 +120,6 @@ hipError_t launch_bwd_delta(const void* out, int out_dtype, const void* dout, in
                             int32_t total_t, int32_t hq, int32_t dv, float* delta,
                             hipStream_t st);
 hipError_t launch_attn_bwd_bf16(const AttnArgs& a, int dqk, int dv, bool causal, bool kv_split,
-                                hipStream_t st);
+                                int total_k, hipStream_t st);
 
 }  // namespace ra

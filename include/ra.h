@@ -253,6 +253,16 @@ ra_status ra_block_attn_bwd(const ra_attn_desc* d, const void* dout, const float
  * j (in a real ring they travel back to it).  out is the final forward
  * output (out_dtype), lse the final lse; delta is computed into the
  * workspace.  dq [total_q, hq, dqk] float32 is added to.
+ *
+ * The workspace (device, caller-owned, ra_rank_backward_workspace bytes;
+ * the same size for every rank of the ring) holds delta [hq, total_q] and
+ * the dK/dV partials of the query split: on blocks with few 128-key tiles,
+ * and on the causal diagonal block, up to 4 workgroups share a key tile,
+ * each taking a contiguous share of its query iterations; share 0 adds into
+ * the owner's dK/dV, shares 1.. store float32 partials in the workspace,
+ * and a reduction adds them in share order (deterministic).  A workspace
+ * smaller than that size is rejected with RA_ERR_INVALID_ARG before any
+ * launch.
  */
 typedef struct ra_rank_bwd_desc {
   ra_attn_desc local;

@@ -196,6 +196,31 @@ def test_rank_forward_workspace_sizes():
     assert n.value == 256 * 4 * 128 * 4
 
 
+@pytest.mark.parametrize("qsplit_env,n_parts", [(None, 1), ("1", 0), ("4", 3)])
+def test_rank_backward_workspace_sizes(qsplit_env, n_parts, monkeypatch):
+    """delta [hq, T] plus the dK/dV partials of the step kind that splits
+    most, the same for every rank: for a 32K GQA rank share (4096 local
+    tokens, 32/8 heads, d 128) the causal diagonal block and the earlier
+    owners' blocks (2048 keys, 128 workgroups of 128 keys) split in two."""
+    if qsplit_env is None:
+        monkeypatch.delenv("RA_BWD_QSPLIT", raising=False)
+    else:
+        monkeypatch.setenv("RA_BWD_QSPLIT", qsplit_env)
+    T, hq, hkv = 4096, 32, 8
+    local = _desc(cu=np.array([0, T], np.int32), hq=hq, hkv=hkv)
+    kb = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    sizes = set()
+    for r in range(8):
+        rd = L.RankBwdDesc()
+        rd.local = local
+        rd.cp_size, rd.rank = 8, r
+        rd.k_blocks = rd.v_blocks = ctypes.cast(kb, ctypes.c_void_p)
+        n = ctypes.c_size_t(0)
+        assert L.lib().ra_rank_backward_workspace(ctypes.byref(rd), ctypes.byref(n)) == 0
+        sizes.add(n.value)
+    assert sizes == {hq * T * 4 + n_parts * T * hkv * (128 + 128) * 4}
+
+
 # ---------------------------------------------------------------------------
 # accounting vs the oracle's pair counts
 # ---------------------------------------------------------------------------
