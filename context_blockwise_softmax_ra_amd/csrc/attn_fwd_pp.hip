@@ -12,8 +12,8 @@
 // A workgroup has 8 waves (256 query rows), i.e. two waves on every SIMD.
 // The two waves of a SIMD take opposite roles and the workgroup alternates
 // between two phases separated by barriers:
-//   phase A: role-A waves run their matrix-core block (P*V of the previous
-//            tile, then S of the current tile) while role-B waves run the
+//   phase A: role-A waves run their matrix-core block (S of the current
+//            tile, then P*V of the previous tile) while role-B waves run the
 //            softmax of their current S on the vector ALU;
 //   phase B: the other way round.
 // So the matrix core of a SIMD is fed by one wave while the other wave's
@@ -24,8 +24,10 @@
 // Both roles run the same code, one phase apart: a role-B wave passes one
 // extra barrier before its first tile and a role-A wave one after its last.
 // Per tile step st a wave runs
-//   [matrix cores: O += V(st-1)^T P(st-1)^T, S(st) = K(st) Q^T]  barrier
+//   [matrix cores: S(st) = K(st) Q^T, O += V(st-1)^T P(st-1)^T]  barrier
 //   [vector ALU:   mask and online softmax of S(st) -> P(st)]     barrier
+// S goes first so that its products have landed when the softmax after the
+// barrier reads them; the P*V results are not read until the next block.
 // so role A computes step st in phases 2st, 2st+1 and role B in phases
 // 2st+1, 2st+2.  Tile t's K is read in phases 2t and 2t+1 and its V in
 // phases 2t+2 and 2t+3, so K and V have separate double buffers.  The
@@ -348,9 +350,9 @@ __global__ __launch_bounds__(PT, 1) void attn_fwd_pp_kernel(AttnArgs a, RankKV r
   // Role-B waves wait for their loads of K(st+1), V(st) at the end of the
   // matrix-core phase, then load K(st+2) into kcur and V(st+1) into vprev.
   auto step = [&](const int st, char* kcur, char* vprev) __attribute__((always_inline)) {
-    if (st >= 1) gemm_pv(vprev);
-    __builtin_amdgcn_sched_barrier(0);
     if (st < total) gemm_s(kcur);
+    __builtin_amdgcn_sched_barrier(0);
+    if (st >= 1) gemm_pv(vprev);
     if (role_b) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     phase_barrier();
     if (role_b) {
