@@ -157,23 +157,31 @@ ra::AttnArgs make_args(const ra_attn_desc* d, const Checked& c) {
 
 // Which bf16 forward kernel runs a launch.  The 8-wave ping-pong kernel
 // works on 256-row query tiles and pays off when its matrix-core phase and
-// softmax phase are of similar length and the tiles are full: head dims
-// 128/128, at least two 256-row tiles (x query heads) per CU of the 256,
-// and at most 1/8 of the tiled rows being padding (short packed documents
-// leave most of a 256-row tile idle).  Otherwise the 4-wave kernel (128-row
-// tiles) runs.  RA_FWD_KERNEL=pp or =4w in the environment forces one.
+// softmax phase are of similar length and the tiles are well filled: head
+// dims 128/128, at least two 256-row tiles (x query heads) per CU of the
+// 256, and at least 3/4 of the tiled rows' work being real rows.  Work
+// weights each segment's rows by its key count, since short packed
+// documents, whose 256-row tiles are mostly padding, carry little of it.
+// (128K packed documents split 16 ways: 70% of the tiled rows are real, 82%
+// of the work, and the ping-pong kernel is 9% faster there.)  Otherwise the
+// 4-wave kernel (128-row tiles) runs.  RA_FWD_KERNEL=pp or =4w in the
+// environment forces one.
 bool use_pingpong(const ra_attn_desc* d, ra_part q_part) {
   const char* e = std::getenv("RA_FWD_KERNEL");
   if (e && !std::strcmp(e, "pp")) return true;
   if (e && !std::strcmp(e, "4w")) return false;
   if (d->dqk != 128 || d->dv != 128) return false;
-  long long tiles = 0, rows = 0;
+  long long tiles = 0;
+  double work = 0.0, tiled_work = 0.0;
   for (int s = 0; s < d->n_seq; ++s) {
     const int lq = part_len(d->cu_seqlens_q_host[s + 1] - d->cu_seqlens_q_host[s], q_part);
-    tiles += (lq + 255) / 256;
-    rows += lq;
+    const double lk = (double)(d->cu_seqlens_k_host[s + 1] - d->cu_seqlens_k_host[s]);
+    const int t = (lq + 255) / 256;
+    tiles += t;
+    work += (double)lq * lk;
+    tiled_work += (double)t * 256.0 * lk;
   }
-  return tiles * d->hq >= 2 * 256 && tiles * 256 * 7 <= rows * 8;
+  return tiles * d->hq >= 2 * 256 && work * 4.0 >= tiled_work * 3.0;
 }
 
 ra_status launch_fwd(const ra_attn_desc* d, const Checked& c, float* out, float* lse, bool merge,

@@ -69,9 +69,11 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
 
   const int nb = gridDim.x;
   const int group = a.group;
-  // causal work only (one causal block, or a rank share of one block):
-  // deal query tiles over the XCDs; otherwise contiguous ranges per XCD
-  const bool causal_only = MODE == 1 || MODE == 3 || (MODE == 2 && rk.cp == 1);
+  // causal work only (one causal block, or a rank share of one block), or a
+  // rank share of packed documents (units of very unequal size, one
+  // document's after another in logical order): deal query tiles over the
+  // XCDs; otherwise contiguous ranges per XCD
+  const bool causal_only = MODE == 1 || MODE == 3 || (MODE == 2 && (rk.cp == 1 || a.n_seq > 1));
   int b = causal_only ? xcd_deal(blockIdx.x, nb, group) : xcd_remap(blockIdx.x, nb);
   const int hg = b % group;
   b /= group;

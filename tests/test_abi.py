@@ -273,7 +273,7 @@ def test_binding_rejects_non_contiguous_buffers():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name,expect", [("tiny_fp32", "attn_fwd_f32"), ("mha_8k", "attn_fwd_bf16"),
-                                         ("gqa_32k", "attn_fwd_pp"), ("varlen_128k", "attn_fwd_bf16"),
+                                         ("gqa_32k", "attn_fwd_pp"), ("varlen_128k", "attn_fwd_pp"),
                                          ("mla_256k", "attn_fwd_bf16")])
 def test_forward_kernel_choice_per_workload(name, expect, monkeypatch):
     monkeypatch.delenv("RA_FWD_KERNEL", raising=False)
@@ -287,6 +287,20 @@ def test_forward_kernel_choice_per_workload(name, expect, monkeypatch):
         assert L.ra_forward_kernel(d, L.PART_ALL) == "attn_fwd_pp"
         monkeypatch.setenv("RA_FWD_KERNEL", "4w")
         assert L.ra_forward_kernel(d, L.PART_ALL) == "attn_fwd_bf16"
+
+
+@pytest.mark.parametrize("lengths,expect", [
+    ([2048] * 4, "attn_fwd_pp"),                  # full 256-row tiles
+    ([128] * 64, "attn_fwd_bf16"),                # every 256-row tile half padding
+    ([8192] + [16] * 256, "attn_fwd_pp"),         # many tiny documents, little of the work
+    ([300] * 32, "attn_fwd_bf16"),                # 300 of 512 tiled rows (59%) real
+])
+def test_forward_kernel_choice_weights_rows_by_work(lengths, expect, monkeypatch):
+    """The ping-pong kernel needs 3/4 of its 256-row tiles' work to be real
+    rows, each segment's rows weighted by its key count."""
+    monkeypatch.delenv("RA_FWD_KERNEL", raising=False)
+    d = _desc(hq=32, hkv=8, cu=synth.cu_seqlens(lengths))
+    assert L.ra_forward_kernel(d, L.PART_ALL) == expect
 
 
 def test_forward_kernel_choice_rejects_bad_input():
