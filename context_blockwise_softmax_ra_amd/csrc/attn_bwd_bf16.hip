@@ -102,7 +102,10 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char vsm[KBN * G::OROWB];
 
   const int nsp = QS ? 1 : a.qsplit;  // workgroups sharing a key tile
-  int b = xcd_remap(blockIdx.x, gridDim.x);
+  // packed documents: deal key tiles (with their query shares) over the
+  // XCDs, since one document's tiles follow another's in logical order;
+  // otherwise contiguous ranges per XCD (neighbours share K/V in L2)
+  int b = a.n_seq > 1 ? xcd_deal(blockIdx.x, gridDim.x, nsp) : xcd_remap(blockIdx.x, gridDim.x);
   const int sp = b % nsp;
   b /= nsp;
   const int kt = b % a.n_ktiles;
@@ -414,7 +417,10 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a) {
   // dO of the workgroup's 128 query rows (dual layout): B operands of dP^T
   __shared__ __attribute__((aligned(1024))) char osm[Q_BM * G::VROWB];
 
-  int b = xcd_remap(blockIdx.x, gridDim.x);
+  // packed documents: deal query tiles (a kv group's heads together) over
+  // the XCDs; otherwise contiguous ranges per XCD
+  int b = a.n_seq > 1 ? xcd_deal(blockIdx.x, gridDim.x, a.group)
+                      : xcd_remap(blockIdx.x, gridDim.x);
   const int hg = b % a.group;
   b /= a.group;
   const int qt_rev = b % a.n_qtiles;
