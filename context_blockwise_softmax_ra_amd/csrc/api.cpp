@@ -757,8 +757,11 @@ static bool bwd_kv_split(const ra_attn_desc* d, const ra::AttnArgs& a) {
 // partials): workgroups of 128 keys, shared by up to kMaxQsplit workgroups
 // that each take a contiguous share of the key tile's query iterations.
 // Split until the launch has 256 workgroups (one per CU), and at least in
-// two on a causal block, whose first key tiles see every query and the last
-// ones only a few.  RA_BWD_QSPLIT=n in the environment forces n.
+// two on a causal block of fewer than 512 workgroups, whose first key tiles
+// see every query and the last ones only a few (with more workgroups than
+// that the heavy-first order already evens the CUs out: the 256K MLA
+// diagonal block, 1024 workgroups, took the same time split).
+// RA_BWD_QSPLIT=n in the environment forces n.
 constexpr int kMaxQsplit = 4;
 static int bwd_qsplit(const ra_attn_desc* d, const Checked& c) {
   const char* e = std::getenv("RA_BWD_QSPLIT");
@@ -766,7 +769,7 @@ static int bwd_qsplit(const ra_attn_desc* d, const Checked& c) {
   const long long wg = (long long)d->n_seq * d->hkv * ((c.max_k_part + 127) / 128);
   int n = 1;
   while (n < kMaxQsplit && wg * n < 256) n *= 2;
-  if (d->causal && n < 2) n = 2;
+  if (d->causal && n < 2 && wg < 512) n = 2;
   return n;
 }
 
