@@ -221,6 +221,32 @@ def test_rank_backward_workspace_sizes(qsplit_env, n_parts, monkeypatch):
     assert sizes == {hq * T * 4 + n_parts * T * hkv * (128 + 128) * 4}
 
 
+def test_rank_backward_rejects_short_workspace(monkeypatch):
+    """A workspace smaller than ra_rank_backward_workspace reports is
+    rejected with RA_ERR_INVALID_ARG before anything is launched (the
+    buffers here are host stand-ins that no kernel could touch)."""
+    monkeypatch.delenv("RA_BWD_QSPLIT", raising=False)
+    T, hq, hkv = 4096, 32, 8
+    local = _desc(cu=np.array([0, T], np.int32), hq=hq, hkv=hkv)
+    kb = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    rd = L.RankBwdDesc()
+    rd.local = local
+    rd.cp_size, rd.rank = 8, 5
+    rd.k_blocks = rd.v_blocks = ctypes.cast(kb, ctypes.c_void_p)
+    rd.dk_blocks = rd.dv_blocks = ctypes.cast(kb, ctypes.c_void_p)
+    rd.out = rd.dout = rd.lse = rd.dq = FAKE
+    rd.out_dtype = L.RA_BF16
+    n = ctypes.c_size_t(0)
+    assert L.lib().ra_rank_backward_workspace(ctypes.byref(rd), ctypes.byref(n)) == 0
+    rd.workspace = FAKE
+    rd.workspace_bytes = n.value - 1
+    assert L.lib().ra_rank_backward(ctypes.byref(rd), None) == L.RA_ERR_INVALID_ARG
+    assert "workspace too small" in L.ra_last_error()
+    rd.workspace = None
+    rd.workspace_bytes = n.value
+    assert L.lib().ra_rank_backward(ctypes.byref(rd), None) == L.RA_ERR_INVALID_ARG
+
+
 # ---------------------------------------------------------------------------
 # accounting vs the oracle's pair counts
 # ---------------------------------------------------------------------------
