@@ -574,8 +574,23 @@ static int fwd_kv_split(const ra_rank_desc* d, const Checked& c) {
   if (e && *e) return std::max(1, std::min(std::atoi(e), kMaxFwdSplit));
   const long long wg = (long long)L.n_seq * L.hkv * (L.hq / L.hkv) *
                        ((c.max_q_part + ra::kFwdBlockM - 1) / ra::kFwdBlockM);
-  if (wg <= 0 || wg >= 256) return 1;
-  return (int)std::min<long long>(8, (512 + wg - 1) / wg);
+  if (wg <= 0) return 1;
+  if (wg < 256) return (int)std::min<long long>(8, (512 + wg - 1) / wg);
+  // Long shares of 1-4 workgroups per slot (two per CU): rows on average
+  // seeing 64K keys or more make the float32 partials a small cost (0.3% of
+  // a 256K MLA share), while halving every unit shortens the tail of the
+  // two-round schedule: that share gains 1.3% (1065 -> 1080 TFLOP/s).  The
+  // 32K GQA share (16K keys per row) loses 5.5% split, so it is not.
+  if (wg < 2048) {
+    double rows = 0.0, keys = 0.0;  // visible keys per row ~ half the global document
+    for (int s = 0; s < L.n_seq; ++s) {
+      const double lq = (double)(L.cu_seqlens_q_host[s + 1] - L.cu_seqlens_q_host[s]);
+      rows += lq;
+      keys += lq * lq * d->cp_size / 2.0;
+    }
+    if (rows > 0.0 && keys >= 65536.0 * rows) return 2;
+  }
+  return 1;
 }
 
 ra_status ra_rank_forward_workspace(const ra_rank_desc* d, size_t* bytes) {

@@ -196,6 +196,38 @@ def test_rank_forward_workspace_sizes():
     assert n.value == 256 * 4 * 128 * 4
 
 
+@pytest.mark.parametrize("name,kernel,parts", [
+    ("mla_256k", None, 2),     # 4-wave kernel, 1024 workgroups, rows see ~131K keys
+    ("gqa_32k", "4w", 0),      # 1024 workgroups but ~16K keys per row: not split
+    ("gqa_32k", None, 0),      # ping-pong kernel: never split
+    ("mha_8k", None, 4),       # 128 workgroups: split to fill the CUs
+])
+def test_fused_forward_kv_split_choice(name, kernel, parts, monkeypatch):
+    """Workspace of a fused rank share = the float32 (out, lse) partials of
+    its KV split parts (none when it is not split)."""
+    monkeypatch.delenv("RA_FWD_KV_SPLIT", raising=False)
+    if kernel is None:
+        monkeypatch.delenv("RA_FWD_KERNEL", raising=False)
+    else:
+        monkeypatch.setenv("RA_FWD_KERNEL", kernel)
+    w = synth.WORKLOADS[name]
+    cu_local, _ = L.ra_zigzag_shard_map(w.cp, 0, w.cu_global())
+    local = _desc(hq=w.hq, hkv=w.hkv, dqk=w.dqk, dv=w.dv, cu=cu_local)
+    kb = (ctypes.c_void_p * w.cp)(*([FAKE] * w.cp))
+    rd = L.RankDesc()
+    rd.local = local
+    rd.cp_size, rd.rank = w.cp, 0
+    rd.k_blocks = rd.v_blocks = ctypes.cast(kb, ctypes.c_void_p)
+    rd.out = rd.lse = FAKE
+    rd.out_dtype = L.RA_BF16
+    rd.fuse_merge = 2
+    n = ctypes.c_size_t(0)
+    assert L.lib().ra_rank_forward_workspace(ctypes.byref(rd), ctypes.byref(n)) == 0
+    T = int(cu_local[-1])
+    align = lambda x: (x + 255) // 256 * 256
+    assert n.value == parts * (align(T * w.hq * w.dv * 4) + align(T * w.hq * 4))
+
+
 @pytest.mark.parametrize("qsplit_env,n_parts", [(None, 1), ("1", 0), ("4", 3)])
 def test_rank_backward_workspace_sizes(qsplit_env, n_parts, monkeypatch):
     """delta [hq, T] plus the dK/dV partials of the step kind that splits
