@@ -793,9 +793,35 @@ static size_t bwd_part_bytes(const ra_attn_desc* d, const Checked& c) {
   return align256((size_t)c.total_k * d->hkv * (d->dqk + d->dv) * sizeof(float));
 }
 
+// dQ key split of a rank-backward step: query tiles of 128 rows shared by up
+// to kMaxQsplit workgroups that deal its key tiles among themselves, doubled
+// until the dQ launch has 256 workgroups (small shares: an 8K MHA rank's
+// history block gives 64-128).  RA_BWD_KSPLIT=n in the environment forces n.
+static int bwd_ksplit(const ra_attn_desc* d, const Checked& c) {
+  const char* e = std::getenv("RA_BWD_KSPLIT");
+  if (e && *e) return std::max(1, std::min(std::atoi(e), kMaxQsplit));
+  const long long wg = (long long)d->n_seq * d->hq * ((c.max_q_part + 127) / 128);
+  int n = 1;
+  while (n < kMaxQsplit && wg * n < 256) n *= 2;
+  return n;
+}
+
+// Bytes of one key share's dQ partial: every query row of the block.
+static size_t bwd_dq_part_bytes(const ra_attn_desc* d, const Checked& c) {
+  return align256((size_t)c.total_q * d->hq * d->dqk * sizeof(float));
+}
+
+// Workspace bytes past delta that a step needs: its dK/dV partials, then
+// its dQ partials.
+static size_t bwd_step_parts(const ra_attn_desc* d, const Checked& c) {
+  return (size_t)(bwd_qsplit(d, c) - 1) * bwd_part_bytes(d, c) +
+         (size_t)(bwd_ksplit(d, c) - 1) * bwd_dq_part_bytes(d, c);
+}
+
 static ra_status launch_bwd(const ra_attn_desc* d, const Checked& c, const void* dout,
                             const float* lse, const float* delta, float* dq, float* dk, float* dv,
-                            hipStream_t st, int qsplit = 1, float* part = nullptr) {
+                            hipStream_t st, int qsplit = 1, float* part = nullptr,
+                            int ksplit = 1, float* dq_part = nullptr) {
   ra::AttnArgs a = make_args(d, c);
   a.n_ktiles = (c.max_k_part + 127) / 128;  // 128-key tiles of the dK/dV kernel
   a.dout = dout;
@@ -808,6 +834,8 @@ static ra_status launch_bwd(const ra_attn_desc* d, const Checked& c, const void*
   a.part_keys = c.total_k;
   a.dk_part = part;
   a.dv_part = part ? part + (size_t)(qsplit - 1) * c.total_k * d->hkv * d->dqk : nullptr;
+  a.ksplit = dq_part ? ksplit : 1;
+  a.dq_part = dq_part;
   // the query-split-over-waves form only where no workspace split runs
   const bool kv_split = a.qsplit == 1 && bwd_kv_split(d, a);
   hipError_t e =
@@ -885,7 +913,7 @@ ra_status ra_rank_backward_workspace(const ra_rank_bwd_desc* d, size_t* bytes) {
     sd.k_part = p.k_part;
     Checked cs;
     if ((st = check_desc(&sd, true, &cs)) != RA_OK) return st;
-    parts = std::max(parts, (size_t)(bwd_qsplit(&sd, cs) - 1) * bwd_part_bytes(&sd, cs));
+    parts = std::max(parts, bwd_step_parts(&sd, cs));
   }
   *bytes = align256((size_t)c.total_q * d->local.hq * sizeof(float)) + parts;
   return ok();
@@ -930,14 +958,17 @@ ra_status ra_rank_backward(const ra_rank_bwd_desc* d, void* stream) {
     int owner;
     if ((st = rank_bwd_step(d, s, &sd, &cs, &owner)) != RA_OK) return st;
     // the partials fit the workspace (sized by ra_rank_backward_workspace)
-    const int qsplit = bwd_qsplit(&sd, cs);
-    if ((size_t)(qsplit - 1) * bwd_part_bytes(&sd, cs) > d->workspace_bytes - delta_b)
-      return fail(RA_ERR_INVALID_ARG, "workspace too small for the dK/dV query split");
+    const int qsplit = bwd_qsplit(&sd, cs), ksplit = bwd_ksplit(&sd, cs);
+    if (bwd_step_parts(&sd, cs) > d->workspace_bytes - delta_b)
+      return fail(RA_ERR_INVALID_ARG, "workspace too small for the dK/dV and dQ splits");
+    float* dq_part = reinterpret_cast<float*>(reinterpret_cast<char*>(part) +
+                                              (size_t)(qsplit - 1) * bwd_part_bytes(&sd, cs));
     if (d->events && d->events[2 * s] &&
         (e = hipEventRecord((hipEvent_t)d->events[2 * s], hs)) != hipSuccess)
       return hip_fail(e, "event record");
     st = launch_bwd(&sd, cs, d->dout, d->lse, delta, d->dq, d->dk_blocks[owner],
-                    d->dv_blocks[owner], hs, qsplit, qsplit > 1 ? part : nullptr);
+                    d->dv_blocks[owner], hs, qsplit, qsplit > 1 ? part : nullptr, ksplit,
+                    ksplit > 1 ? dq_part : nullptr);
     if (st != RA_OK) return st;
     if (d->events && d->events[2 * s + 1] &&
         (e = hipEventRecord((hipEvent_t)d->events[2 * s + 1], hs)) != hipSuccess)

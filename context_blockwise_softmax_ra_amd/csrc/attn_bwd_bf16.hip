@@ -417,10 +417,13 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a) {
   // dO of the workgroup's 128 query rows (dual layout): B operands of dP^T
   __shared__ __attribute__((aligned(1024))) char osm[Q_BM * G::VROWB];
 
-  // packed documents: deal query tiles (a kv group's heads together) over
-  // the XCDs; otherwise contiguous ranges per XCD
-  int b = a.n_seq > 1 ? xcd_deal(blockIdx.x, gridDim.x, a.group)
+  // packed documents: deal query tiles (a kv group's heads and their key
+  // shares together) over the XCDs; otherwise contiguous ranges per XCD
+  const int nks = max(a.ksplit, 1);  // workgroups sharing a query tile
+  int b = a.n_seq > 1 ? xcd_deal(blockIdx.x, gridDim.x, a.group * nks)
                       : xcd_remap(blockIdx.x, gridDim.x);
+  const int kshare = b % nks;  // this workgroup takes key tiles kshare, kshare + nks, ...
+  b /= nks;
   const int hg = b % a.group;
   b /= a.group;
   const int qt_rev = b % a.n_qtiles;
@@ -539,37 +542,85 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a) {
     pipeline_lds_mfma<4 * G::NQT, 2, kBwdAhead>();
   };
 
-  if (ntiles > 0) issue(0, ks0, vs0);
+  // this workgroup's key tiles: j-th is tile kshare + j * nks
+  const int n_mine = ntiles > kshare ? (ntiles - kshare + nks - 1) / nks : 0;
+  if (n_mine > 0) issue(kshare, ks0, vs0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  auto step = [&](int t, const char* ks, const char* vs, char* kn, char* vn)
+  auto step = [&](int j, const char* ks, const char* vs, char* kn, char* vn)
       __attribute__((always_inline)) {
-    if (t + 1 < ntiles) issue(t + 1, kn, vn);
-    tile(t, ks, vs);
+    if (j + 1 < n_mine) issue(kshare + (j + 1) * nks, kn, vn);
+    tile(kshare + j * nks, ks, vs);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, ks0, vs0, ks1, vs1);
-    if (t + 1 < ntiles) step(t + 1, ks1, vs1, ks0, vs0);
+  for (int j = 0; j < n_mine; j += 2) {
+    step(j, ks0, vs0, ks1, vs1);
+    if (j + 1 < n_mine) step(j + 1, ks1, vs1, ks0, vs0);
   }
   if (!wave_live || !row_ok) return;
 
   // C: column = query row (this lane), rows = dims 32*nt + 8*(i/4) + 4g + i%4
-  float* dqp = a.dq + ((int64_t)my_row * a.hq + h) * DQK;
   const float scale = a.scale;
+  if (kshare == 0) {
+    float* dqp = a.dq + ((int64_t)my_row * a.hq + h) * DQK;
 #pragma unroll
-  for (int nt = 0; nt < G::NQT; ++nt)
+    for (int nt = 0; nt < G::NQT; ++nt)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      float4* p = reinterpret_cast<float4*>(dqp + 32 * nt + 8 * q4 + 4 * g);
-      float4 x = *p;
-      x.x += scale * dq[nt][4 * q4 + 0];
-      x.y += scale * dq[nt][4 * q4 + 1];
-      x.z += scale * dq[nt][4 * q4 + 2];
-      x.w += scale * dq[nt][4 * q4 + 3];
-      *p = x;
-    }
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float4* p = reinterpret_cast<float4*>(dqp + 32 * nt + 8 * q4 + 4 * g);
+        float4 x = *p;
+        x.x += scale * dq[nt][4 * q4 + 0];
+        x.y += scale * dq[nt][4 * q4 + 1];
+        x.z += scale * dq[nt][4 * q4 + 2];
+        x.w += scale * dq[nt][4 * q4 + 3];
+        *p = x;
+      }
+  } else {
+    float* dqp = a.dq_part + (((int64_t)(kshare - 1) * a.total_q + my_row) * a.hq + h) * DQK;
+#pragma unroll
+    for (int nt = 0; nt < G::NQT; ++nt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float4 x;
+        x.x = scale * dq[nt][4 * q4 + 0];
+        x.y = scale * dq[nt][4 * q4 + 1];
+        x.z = scale * dq[nt][4 * q4 + 2];
+        x.w = scale * dq[nt][4 * q4 + 3];
+        *reinterpret_cast<float4*>(dqp + 32 * nt + 8 * q4 + 4 * g) = x;
+      }
+  }
+}
+
+// dq += the stored partials of key shares 1 .. ksplit-1, in share order,
+// for every row the dQ launch covered (rows inside the q part of a segment
+// whose k part is not empty).  One thread per 4 floats of a row's
+// [hq, dqk] gradient; HBM-bound.
+__global__ __launch_bounds__(256) void bwd_ksplit_reduce_kernel(AttnArgs a, int dqk) {
+  const int row4 = a.hq * dqk / 4;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)a.total_q * row4) return;
+  const int row = (int)(idx / row4), c = (int)(idx % row4);
+  int lo = 0, hi = a.n_seq;  // segment of the row: cu_q[seg] <= row < cu_q[seg + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.cu_q[mid] <= row) lo = mid; else hi = mid;
+  }
+  int q_lo, q_hi, k_lo, k_hi;
+  part_range(a.cu_q[lo], a.cu_q[lo + 1], a.q_part, &q_lo, &q_hi);
+  part_range(a.cu_k[lo], a.cu_k[lo + 1], a.k_part, &k_lo, &k_hi);
+  if (k_hi <= k_lo || row < q_lo || row >= q_hi) return;
+  const int64_t off = (int64_t)row * a.hq * dqk + 4 * c;
+  const int64_t stride = (int64_t)a.total_q * a.hq * dqk;
+  float4 acc = *reinterpret_cast<const float4*>(a.dq + off);
+  for (int s = 1; s < a.ksplit; ++s) {
+    const float4 x = *reinterpret_cast<const float4*>(a.dq_part + (s - 1) * stride + off);
+    acc.x += x.x;
+    acc.y += x.y;
+    acc.z += x.z;
+    acc.w += x.w;
+  }
+  *reinterpret_cast<float4*>(a.dq + off) = acc;
 }
 
 }  // namespace
@@ -579,7 +630,8 @@ hipError_t launch_attn_bwd_bf16(const AttnArgs& a0, int dqk, int dv, bool causal
   // a0.n_qtiles counts 128-row query tiles, a0.n_ktiles 128-key tiles; with
   // kv_split (d_qk = 128 only) the dK/dV kernel runs 32-key workgroups
   AttnArgs a = a0;
-  const long long nq = (long long)a.n_seq * a.hkv * a.n_qtiles * a.group;
+  if (a.ksplit < 1 || !a.dq_part) a.ksplit = 1;
+  const long long nq = (long long)a.n_seq * a.hkv * a.n_qtiles * a.group * a.ksplit;
   AttnArgs ak = a;
   if (kv_split) ak.n_ktiles = 4 * a.n_ktiles;
   if (kv_split || ak.qsplit < 1) ak.qsplit = 1;
@@ -610,6 +662,13 @@ hipError_t launch_attn_bwd_bf16(const AttnArgs& a0, int dqk, int dv, bool causal
     return hipErrorInvalidValue;
   }
 #undef RA_BWD_LAUNCH
+  if (a.ksplit > 1 && nq > 0) {
+    const long long n4 = (long long)a.total_q * a.hq * dqk / 4;
+    const long long nb = (n4 + 255) / 256;
+    if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (nb > 0)
+      hipLaunchKernelGGL(bwd_ksplit_reduce_kernel, dim3((unsigned)nb), dim3(256), 0, st, a, dqk);
+  }
   if (ak.qsplit > 1 && nk > 0) {
     const long long n4 = (long long)total_k * a.hkv * (dqk + dv) / 4;
     const long long nb = (n4 + 255) / 256;

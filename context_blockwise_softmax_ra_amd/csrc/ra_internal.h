@@ -55,6 +55,12 @@ struct AttnArgs {
   int32_t part_keys;
   float* dk_part;
   float* dv_part;
+  // dQ key split: ksplit workgroups share each query tile, dealing its key
+  // tiles round-robin; share 0 adds into dq, share s > 0 stores its scaled
+  // partial at dq_part + (s - 1) * total_q rows, which bwd_ksplit_reduce
+  // adds in share order.
+  int32_t ksplit;
+  float* dq_part;
 };
 
 // KV blocks of every owner for a rank's fused forward (one launch per rank).

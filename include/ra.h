@@ -260,7 +260,10 @@ ra_status ra_block_attn_bwd(const ra_attn_desc* d, const void* dout, const float
  * and on the causal diagonal block, up to 4 workgroups share a key tile,
  * each taking a contiguous share of its query iterations; share 0 adds into
  * the owner's dK/dV, shares 1.. store float32 partials in the workspace,
- * and a reduction adds them in share order (deterministic).  A workspace
+ * and a reduction adds them in share order (deterministic).  Likewise, on
+ * blocks with few 128-row query tiles, up to 4 workgroups share a query
+ * tile for dQ, dealing its key tiles; share 0 adds into dq, the others'
+ * float32 partials follow the dK/dV ones in the workspace.  A workspace
  * smaller than that size is rejected with RA_ERR_INVALID_ARG before any
  * launch.
  */
