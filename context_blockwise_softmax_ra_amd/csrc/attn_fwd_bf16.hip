@@ -49,6 +49,12 @@ namespace {
 using namespace mfma;
 using namespace fwd;
 
+// Lazy-rescale threshold (log2 units) of the d_qk = 192 softmax below, the
+// same as online_softmax_tile's: the running max is raised only when a
+// row's max grows by more than this; numerator, row sum and lse use the
+// same (possibly stale) max, so the result is exact.
+constexpr float kRescaleLog2 = 8.0f;
+
 constexpr int BM = kFwdBlockM;
 constexpr int NW = kFwdWaves;
 constexpr int NT = NW * 64;
@@ -318,7 +324,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
 #pragma unroll
         for (int i = 1; i < 15; i += 2) mx = mx3(mx, s[1][i], s[1][i + 1]);
         mx = xhalf_max(fmaxf(mx, s[1][15]));
-        const bool raise = (mx - m_run) * c2 > 8.0f;  // true on the first live tile
+        const bool raise = (mx - m_run) * c2 > kRescaleLog2;  // true on the first live tile
         if (__builtin_amdgcn_ballot_w64(raise)) {
           const float m_new = raise ? mx : m_run;
           const float m_use_new = (m_new == -INFINITY) ? 0.f : m_new;
