@@ -593,6 +593,23 @@ static int fwd_kv_split(const ra_rank_desc* d, const Checked& c) {
   return 1;
 }
 
+// Half tiles (ping-pong kernel, fused rank share of packed documents):
+// tile each zig-zag chunk of a document on its own.  A 256-row tile that
+// straddles a document's two chunks runs the later owners' blocks, which
+// only the second chunk sees, with its first-chunk waves idle; separate
+// tiles skip those blocks whole, at the price of more padding.  So they pay
+// off on ranks that have later owners (rank < C - 1): on the 128K mix at
+// CP 16 ranks 0-13 ran 4-8% faster, rank 14 the same, rank 15 1-3% slower,
+// the step 530 -> 563 TFLOP/s with them on every rank.  A single sequence
+// splits into whole tiles either way.  RA_FWD_HALF_TILES=0/1 in the
+// environment forces the choice.
+static bool fwd_half_tiles(const ra_rank_desc* d) {
+  const char* e = std::getenv("RA_FWD_HALF_TILES");
+  if (e && !std::strcmp(e, "1")) return true;
+  if (e && !std::strcmp(e, "0")) return false;
+  return d->local.n_seq > 1 && d->rank < d->cp_size - 1;
+}
+
 ra_status ra_rank_forward_workspace(const ra_rank_desc* d, size_t* bytes) {
   if (!d || !bytes) return fail(RA_ERR_INVALID_ARG, "NULL argument");
   Checked c;
@@ -668,11 +685,21 @@ ra_status ra_rank_forward(const ra_rank_desc* d, void* stream) {
       a.out = static_cast<float*>(d->workspace);
       a.lse = reinterpret_cast<float*>(static_cast<char*>(d->workspace) + split * out_b);
     }
+    const bool pp = use_pingpong(&L, RA_PART_ALL);
+    if (pp && fwd_half_tiles(d)) {
+      int nh = 0;
+      for (int s = 0; s < L.n_seq; ++s) {
+        const int half = (L.cu_seqlens_q_host[s + 1] - L.cu_seqlens_q_host[s]) / 2;
+        nh = std::max(nh, 2 * ((half + 255) / 256));
+      }
+      a.half_tiles = 1;
+      a.n_qtiles_half = nh;
+    }
     if (d->events && d->events[0] &&
         (e = hipEventRecord((hipEvent_t)d->events[0], hs)) != hipSuccess)
       return hip_fail(e, "event record");
     if (a.n_qtiles > 0) {
-      e = use_pingpong(&L, RA_PART_ALL)
+      e = pp
               ? ra::launch_rank_fwd_pp(a, rk, L.dqk, L.dv, d->out_dtype == RA_BF16, hs)
               : ra::launch_rank_fwd_bf16(a, rk, L.dqk, L.dv,
                                          split == 1 && d->out_dtype == RA_BF16, hs);

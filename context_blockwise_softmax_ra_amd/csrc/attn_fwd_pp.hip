@@ -105,9 +105,20 @@ __global__ __launch_bounds__(PT, 1) void attn_fwd_pp_kernel(AttnArgs a, RankKV r
 
   int q_lo, q_hi;
   part_range(a.cu_q[seg], a.cu_q[seg + 1], MODE == 2 ? RA_PART_ALL : a.q_part, &q_lo, &q_hi);
-  const int q0 = q_lo + qt * PBM;
-  if (q0 >= q_hi) return;  // whole workgroup
   const int qhalf = (q_hi - q_lo) >> 1;
+  // the tile's rows [q0, t_hi): tiles over the whole segment, or (half
+  // tiles) over each zig-zag chunk on its own, so that no tile straddles
+  // the two and blocks seen by the second chunk only skip whole tiles
+  int q0 = q_lo + qt * PBM, t_hi = q_hi;
+  if (MODE == 2 && a.half_tiles) {
+    const int nh = (qhalf + PBM - 1) / PBM;
+    if (qt < nh) {
+      t_hi = q_lo + qhalf;
+    } else {
+      q0 = q_lo + qhalf + (qt - nh) * PBM;
+    }
+  }
+  if (q0 >= t_hi) return;  // whole workgroup
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -115,11 +126,11 @@ __global__ __launch_bounds__(PT, 1) void attn_fwd_pp_kernel(AttnArgs a, RankKV r
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
-  const int qrel_last_wg = min(q0 + PBM, q_hi) - 1 - q_lo;
+  const int qrel_last_wg = min(q0 + PBM, t_hi) - 1 - q_lo;
   const int wq0 = q0 + wave * kFwdRowsPerWave;
-  const bool wave_live = wq0 < q_hi;
+  const bool wave_live = wq0 < t_hi;
   const int wq_first_rel = wq0 - q_lo;
-  const int wq_last_rel = min(wq0 + kFwdRowsPerWave, q_hi) - 1 - q_lo;
+  const int wq_last_rel = min(wq0 + kFwdRowsPerWave, t_hi) - 1 - q_lo;
   const int my_row = wq0 + l32;
   const int my_row_rel = my_row - q_lo;
   const int64_t ks_bytes = a.k_stride * 2, vs_bytes = a.v_stride * 2;
@@ -234,7 +245,7 @@ __global__ __launch_bounds__(PT, 1) void attn_fwd_pp_kernel(AttnArgs a, RankKV r
   bf16x8 qf[G::KK];
   {
     const __bf16* qb = reinterpret_cast<const __bf16*>(a.q) + (int64_t)h * DQK;
-    const int row = min(my_row, q_hi - 1);
+    const int row = min(my_row, t_hi - 1);
     const __bf16* qp = qb + (int64_t)row * a.q_stride + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < G::KK; ++kk) qf[kk] = as_bf16x8(ldg16(qp + 16 * kk));
@@ -370,7 +381,7 @@ __global__ __launch_bounds__(PT, 1) void attn_fwd_pp_kernel(AttnArgs a, RankKV r
   }
   if (!role_b) phase_barrier();
 
-  if (!wave_live || my_row >= q_hi) return;
+  if (!wave_live || my_row >= t_hi) return;
 
   // ---- epilogue: lanes l and l^32 hold the two key halves of the same row
   const float l_tot = xhalf_sum(l_run);
@@ -437,8 +448,9 @@ __global__ __launch_bounds__(PT, 1) void attn_fwd_pp_kernel(AttnArgs a, RankKV r
 template <int DQK, int DV>
 hipError_t launch_pp_t(const AttnArgs& a, const RankKV* rk, bool causal, bool merge,
                        bool out_bf16, hipStream_t st) {
-  // query tiles of 256 rows from the 128-row count the host computed
-  const int nq = (a.n_qtiles + 1) / 2;
+  // query tiles of 256 rows from the 128-row count the host computed, or
+  // the host's count of half tiles
+  const int nq = (rk && a.half_tiles) ? a.n_qtiles_half : (a.n_qtiles + 1) / 2;
   const long long nblk = (long long)a.n_seq * a.hkv * nq * a.group;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;

@@ -61,6 +61,11 @@ struct AttnArgs {
   // adds in share order.
   int32_t ksplit;
   float* dq_part;
+  // fused rank share on the ping-pong kernel: tile the two halves (zig-zag
+  // chunks) of every segment separately, n_qtiles_half 256-row tiles per
+  // segment at most
+  int32_t half_tiles;
+  int32_t n_qtiles_half;
 };
 
 // KV blocks of every owner for a rank's fused forward (one launch per rank).
