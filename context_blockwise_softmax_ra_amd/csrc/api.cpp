@@ -36,6 +36,20 @@ ra_status ok() {
   return RA_OK;
 }
 
+}  // namespace
+
+ra_status ra::set_error(ra_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+namespace {
+
 ra_status hip_fail(hipError_t e, const char* what) {
   return fail(RA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -273,6 +287,10 @@ ra_status check_rank_common(const ra_attn_desc& L, int cp, int rank, const void*
   for (int s = 0; s <= L.n_seq; ++s)
     if (L.cu_seqlens_q_host[s] != L.cu_seqlens_k_host[s])
       return fail(RA_ERR_INVALID_ARG, "local q and k cu_seqlens must match");
+  // a rank's local buffers start at its first row: the KV-split combine,
+  // the cast and delta run over rows [0, cu[n_seq])
+  if (L.cu_seqlens_q_host[0] != 0)
+    return fail(RA_ERR_INVALID_ARG, "local cu_seqlens must start at 0");
   if (cp > 1)
     for (int s = 0; s < L.n_seq; ++s)
       if ((L.cu_seqlens_q_host[s + 1] - L.cu_seqlens_q_host[s]) & 1)
@@ -687,10 +705,14 @@ ra_status ra_rank_forward(const ra_rank_desc* d, void* stream) {
     }
     const bool pp = use_pingpong(&L, RA_PART_ALL);
     if (pp && fwd_half_tiles(d)) {
+      // tiles of the first chunk (len/2 rows) plus those of the second
+      // (len - len/2 rows; one more than the first when a cp_size = 1
+      // share has an odd length)
       int nh = 0;
       for (int s = 0; s < L.n_seq; ++s) {
-        const int half = (L.cu_seqlens_q_host[s + 1] - L.cu_seqlens_q_host[s]) / 2;
-        nh = std::max(nh, 2 * ((half + 255) / 256));
+        const int len = L.cu_seqlens_q_host[s + 1] - L.cu_seqlens_q_host[s];
+        const int half = len / 2;
+        nh = std::max(nh, (half + 255) / 256 + (len - half + 255) / 256);
       }
       a.half_tiles = 1;
       a.n_qtiles_half = nh;

@@ -133,4 +133,7 @@ hipError_t launch_bwd_delta(const void* out, int out_dtype, const void* dout, in
 hipError_t launch_attn_bwd_bf16(const AttnArgs& a, int dqk, int dv, bool causal, bool kv_split,
                                 int total_k, hipStream_t st);
 
+// Sets the thread-local message ra_last_error() returns and passes st back.
+ra_status set_error(ra_status st, const char* fmt, ...);
+
 }  // namespace ra

@@ -90,7 +90,8 @@ class RingProblem:
         dev = self.q[0].device
         out = torch.empty((self.Tl, self.hq, self.dv), dtype=out_dtype, device=dev)
         lse = torch.empty((self.hq, self.Tl), dtype=torch.float32, device=dev)
-        # the KV split (and so the workspace) can differ by rank: size for all
+        # the split rule reads shapes only, so every rank reports the same
+        # size; the max over ranks is defensive
         n = max(L.ra_rank_forward_workspace(self.forward_desc(r, out, lse, None, fuse_merge))
                 for r in range(self.cp))
         ws = torch.empty(max(n, 16), dtype=torch.uint8, device=dev)

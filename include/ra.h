@@ -20,6 +20,9 @@
  *   - "超长上下文训练速度翻倍秘籍" (ant-ling), section 2, "踩坑一": the
  *     diagonal block (local Q x local KV) is causal; received history KV
  *     blocks are fully visible and use a non-causal call.
+ *   - "seq_len 从 4K 推到 16K、CP=2 一开就慢了 20%：Ulysses Context
+ *     Parallelism 的工程取舍全记录" (iqiancheng), section 1.1: KV blocks
+ *     travel device 0 -> 1 -> ... -> C-1 -> 0 round the ring.
  *
  * Conventions for every entry point:
  *   - Layout: token-major packed tensors [tokens, heads, dim] with dim
@@ -176,7 +179,7 @@ ra_status ra_cast_f32_bf16(const float* src, void* dst, int64_t n, void* stream)
  * rank's local Q (k, v ignored) and the local cu_seqlens, which are the
  * same for the rank's own KV block and every received one.  At step s the
  * block of owner j = (rank - s) mod cp_size is used (KV moves rank 0 -> 1
- * -> ... as in the iqiancheng page, section 1.1):
+ * -> ... as in the iqiancheng page cited above, section 1.1):
  *   s = 0      : causal, all local rows x all keys (the diagonal block);
  *   j < rank   : non-causal, all rows x FIRST half of the owner's keys;
  *   j > rank   : non-causal, SECOND half of the rows x all the owner's keys
@@ -194,16 +197,19 @@ ra_status ra_cast_f32_bf16(const float* src, void* dst, int64_t n, void* stream)
  * 2 (bf16): the whole share in one launch, every owner's block walked in
  * ring order with the online-softmax state kept in registers and the final
  * output written by the epilogue (the pass-KV form of the oh-bug page with
- * all blocks resident; no workspace).  A share too small to give every CU
- * a workgroup (fewer than 256 of 128 rows x one query head, 4-wave kernel)
- * is split instead: its key tiles (over all blocks, in ring order) are
- * dealt round-robin over up to 8 parts, each part's workgroups write a
- * float32 partial (out, lse) into the workspace, and a combine launch
- * weights the parts by their lse in part order (deterministic).  The workspace is then parts x (out + lse);
- * ra_rank_forward_workspace reports it (0 without a split).  The
- * environment variable RA_FWD_KV_SPLIT=<n> forces n parts (1 = none, at
- * most 16).
- * fp32 falls back to 1.
+ * all blocks resident).  On the 4-wave kernel a share may be split instead:
+ * its key tiles (over all blocks, in ring order) are dealt round-robin over
+ * several parts, each part's workgroups write a float32 partial (out, lse)
+ * into the workspace, and a combine launch weights the parts by their lse
+ * in part order (deterministic).  The split is taken when the share has
+ * fewer than 256 workgroups (128 rows x one query head; up to 8 parts), and
+ * in 2 parts when it has 256-2047 workgroups whose rows see on average 64K
+ * keys or more (long shares such as 256K MLA).  The workspace is then
+ * parts x (out + lse), otherwise 0; since the rule depends on the shapes,
+ * callers must always ask ra_rank_forward_workspace for the size (it is the
+ * same for every rank of a ring).  The environment variable
+ * RA_FWD_KV_SPLIT=<n> forces n parts (1 = none, at most 16).
+ * fp32 falls back to fuse_merge = 1.
  * events (optional): host array of 2*cp_size hipEvent_t, recorded on the
  * stream right before / after step s's attention launch (with
  * fuse_merge = 2 only events[0], events[1], around the launch and its
@@ -378,9 +384,10 @@ ra_status ra_segments_work(const ra_segment* segs, int32_t n_seg, int32_t hq,
  * fuse_merge = 2 and RA_PART_ALL): "attn_fwd_pp" (8 waves, 256-row query
  * tiles, matrix-core and softmax phases of the two waves of a SIMD
  * interleaved) for head dims 128/128 when the launch has at least 512 such
- * tiles over all query heads and at most 1/8 of the tiled rows are padding,
- * "attn_fwd_bf16" (4 waves, 128-row tiles) otherwise, "attn_fwd_f32" for
- * float32.  Both bf16 kernels compute the same result.  The environment
+ * tiles over all query heads and real rows carry at least 3/4 of the tiled
+ * rows' work, each segment's rows weighted by its key count (so padding in
+ * the tiles of short segments counts little), "attn_fwd_bf16" (4 waves,
+ * 128-row tiles) otherwise, "attn_fwd_f32" for float32.  Both bf16 kernels compute the same result.  The environment
  * variable RA_FWD_KERNEL=pp or =4w forces one.  Host only; NULL (with
  * ra_last_error set) for an invalid descriptor.
  */

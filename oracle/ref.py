@@ -28,7 +28,8 @@ Sources (pages of the subject, cited by title and section):
   * "超长上下文训练速度翻倍秘籍" (ant-ling), section 2 "踩坑一" (the diagonal
     block is local Q x local KV under the causal mask; received history
     blocks are fully visible and use a non-causal call).
-  * "Ulysses vs Ring Attention" (iqiancheng), section 1.1 (KV blocks move
+  * "seq_len 从 4K 推到 16K、CP=2 一开就慢了 20%：Ulysses Context
+    Parallelism 的工程取舍全记录" (iqiancheng), section 1.1 (KV blocks move
     device 0 -> 1 -> ... -> C-1 -> 0).
   * The oh-bug correctness section on causal rank imbalance also names the
     other placements implemented in ``map_local_tokens`` (striped /
@@ -495,7 +496,3 @@ def bf16_round_bits(x_f32: np.ndarray) -> np.ndarray:
     nan = np.isnan(np.asarray(x_f32, dtype=np.float32))
     r = np.where(nan, ((u >> 16) | 0x40) & 0xFFFF, r)
     return r.astype(np.uint16)
-
-
-def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
-    return (np.asarray(bits, dtype=np.uint32) << 16).astype(np.uint32).view(np.float32).astype(np.float64)

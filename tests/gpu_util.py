@@ -94,3 +94,84 @@ def sample_rows(prob, r: int, n: int, seed: int = 0) -> np.ndarray:
     while len(pick) < min(n, prob.Tl):
         pick.add(int(rng.integers(0, prob.Tl)))
     return np.array(sorted(pick), dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# Oracle references at full size: the oracle's own functions, called once per
+# query head on a thread pool (NumPy and BLAS release the GIL; BLAS is held
+# to one thread per call so the pool does not oversubscribe the cores).
+# ---------------------------------------------------------------------------
+
+def _pool_workers() -> int:
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _per_head(fn, n):
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        with ThreadPoolExecutor(_pool_workers()) as ex:
+            return list(ex.map(fn, range(n)))
+
+
+def _runs(rows: np.ndarray, lay) -> list:
+    """Split sorted global rows into runs of consecutive tokens of one document."""
+    out, start = [], 0
+    for i in range(1, len(rows) + 1):
+        if (i == len(rows) or rows[i] != rows[i - 1] + 1
+                or lay.doc[rows[i]] != lay.doc[rows[i - 1]]):
+            out.append((start, i))
+            start = i
+    return out
+
+
+def oracle_rows(q64, k64, v64, cu, rows):
+    """oracle.attention of the given global rows (sorted) over every key they
+    can see, per query head.  Each run of consecutive rows of one document
+    is passed the keys from its document's start to the run's last row: a
+    superset of every row's visible keys (the oracle masks the rest), so
+    the result is the oracle's full attention of those rows."""
+    rows = np.asarray(rows, dtype=np.int64)
+    lay = oracle.ref.Layout(cu)
+    hq, hkv = q64.shape[1], k64.shape[1]
+    grp = hq // hkv
+    runs = _runs(rows, lay)
+
+    def head(h):
+        g = h // grp
+        o = np.zeros((len(rows), 1, v64.shape[2]))
+        l = np.zeros((1, len(rows)))
+        for a, b in runs:
+            r0, r1 = int(rows[a]), int(rows[b - 1]) + 1      # consecutive tokens
+            k0 = int(lay.cu[lay.doc[r0]])
+            o[a:b], l[:, a:b] = oracle.attention(q64[r0:r1, h:h + 1], k64[k0:r1, g:g + 1],
+                                                 v64[k0:r1, g:g + 1], lay.pos[r0:r1],
+                                                 lay.doc[r0:r1], lay.pos[k0:r1], lay.doc[k0:r1])
+        return o, l
+
+    res = _per_head(head, hq)
+    return (np.concatenate([o for o, _ in res], axis=1),
+            np.concatenate([l for _, l in res], axis=0))
+
+
+def oracle_grads(q64, k64, v64, do64, cu):
+    """oracle.attention_bwd of the whole stream (every row over every key),
+    one query head at a time; query heads of a group add their dK, dV."""
+    lay = oracle.ref.Layout(cu)
+    hq, hkv = q64.shape[1], k64.shape[1]
+    grp = hq // hkv
+
+    def head(h):
+        g = h // grp
+        return oracle.attention_bwd(q64[:, h:h + 1], k64[:, g:g + 1], v64[:, g:g + 1],
+                                    do64[:, h:h + 1], lay.pos, lay.doc, lay.pos, lay.doc)
+
+    res = _per_head(head, hq)
+    dq = np.concatenate([a for a, _, _ in res], axis=1)
+    dk = np.zeros_like(k64)
+    dv = np.zeros_like(v64)
+    for h, (_, b, c) in enumerate(res):
+        dk[:, h // grp:h // grp + 1] += b
+        dv[:, h // grp:h // grp + 1] += c
+    return dq, dk, dv

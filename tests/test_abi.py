@@ -178,6 +178,37 @@ def test_rank_forward_validation():
     assert L.lib().ra_rank_forward(ctypes.byref(rd), None) == L.RA_ERR_INVALID_ARG
 
 
+def test_rank_calls_reject_local_rows_not_starting_at_zero():
+    """A rank's local buffers start at row 0: the split combine, the cast and
+    delta cover rows [0, cu[n_seq]), so a local cu_seqlens with cu[0] > 0
+    (rows no kernel would write) is rejected before any launch, by the
+    forward, the backward and both workspace queries."""
+    cu = np.array([16, 272], dtype=np.int32)
+    local = _desc(cu=cu, hq=4, hkv=2)
+    kb = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    rd = L.RankDesc()
+    rd.local = local
+    rd.cp_size, rd.rank = 2, 0
+    rd.k_blocks = rd.v_blocks = ctypes.cast(kb, ctypes.c_void_p)
+    rd.out = rd.lse = FAKE
+    rd.out_dtype = L.RA_BF16
+    n = ctypes.c_size_t(0)
+    for fm in (0, 1, 2):
+        rd.fuse_merge = fm
+        assert L.lib().ra_rank_forward_workspace(ctypes.byref(rd), ctypes.byref(n)) == \
+            L.RA_ERR_INVALID_ARG
+        assert "start at 0" in L.ra_last_error()
+        assert L.lib().ra_rank_forward(ctypes.byref(rd), None) == L.RA_ERR_INVALID_ARG
+    bd = L.RankBwdDesc()
+    bd.local = local
+    bd.cp_size, bd.rank = 2, 0
+    bd.k_blocks = bd.v_blocks = ctypes.cast(kb, ctypes.c_void_p)
+    assert L.lib().ra_rank_backward_workspace(ctypes.byref(bd), ctypes.byref(n)) == \
+        L.RA_ERR_INVALID_ARG
+    assert L.lib().ra_rank_backward(ctypes.byref(bd), None) == L.RA_ERR_INVALID_ARG
+    assert "start at 0" in L.ra_last_error()
+
+
 def test_rank_forward_workspace_sizes():
     cu = np.array([0, 256], dtype=np.int32)
     local = _desc(cu=cu, hq=4, hkv=2)

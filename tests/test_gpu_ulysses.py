@@ -2,8 +2,9 @@
 
 After the all-to-all of Ulysses sequence parallelism a rank holds every
 token of Hq/C query heads and Hkv/C kv heads; its share is causal
-attention over the whole sequence for those heads ("Ulysses vs Ring
-Attention", section 1.2).  It runs as ra_rank_forward with cp_size = 1 over
+attention over the whole sequence for those heads ("seq_len 从 4K 推到
+16K、CP=2 一开就慢了 20%：Ulysses Context Parallelism 的工程取舍全记录",
+section 1.2).  It runs as ra_rank_forward with cp_size = 1 over
 a head slice of the global buffers, i.e. on the ring share's kernels.  The
 oracle's full attention restricted to the rank's heads is the reference.
 """
@@ -103,3 +104,28 @@ def test_ulysses_rejects_head_counts_not_divisible():
     z = torch.zeros((64, w.hq, 64), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(ValueError):
         UlyssesProblem(z, z, z, np.array([0, 64], np.int32), w.cp)
+
+
+@pytest.mark.parametrize("lengths", [[513, 300, 7], [1023, 1, 256, 511]])
+def test_ulysses_share_odd_lengths_with_half_tiles(lengths, monkeypatch):
+    """A cp_size = 1 share may hold odd-length documents.  With half tiles
+    forced on the ping-pong kernel, a document's second chunk has one row
+    more than its first (len - len/2); e.g. 513 = 256 + 257 needs 1 + 2
+    tiles.  Every row must be written and match the oracle."""
+    monkeypatch.setenv("RA_FWD_KERNEL", "pp")
+    monkeypatch.setenv("RA_FWD_HALF_TILES", "1")
+    cu = synth.cu_seqlens(lengths)
+    T = int(cu[-1])
+    g = torch.Generator().manual_seed(sum(lengths))
+    q = torch.randn(T, 4, 128, generator=g).to(torch.bfloat16)
+    k = torch.randn(T, 2, 128, generator=g).to(torch.bfloat16)
+    v = torch.randn(T, 2, 128, generator=g).to(torch.bfloat16)
+    prob = UlyssesProblem(q.to(DEV), k.to(DEV), v.to(DEV), cu, 1)
+    out, lse, ws = prob.alloc_forward()
+    out.fill_(float("nan"))
+    lse.fill_(float("nan"))
+    prob.forward(0, out, lse, ws)
+    torch.cuda.synchronize()
+    ro, rl = oracle.full_attention(to_np(q), to_np(k), to_np(v), cu)
+    check_out(to_np(out), ro, "bf16", f"odd lengths {lengths}")
+    check_lse(to_np(lse), rl, f"odd lengths {lengths}")
