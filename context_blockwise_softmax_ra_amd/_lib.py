@@ -27,7 +27,7 @@ _STATUS = {0: "RA_OK", 1: "RA_ERR_INVALID_ARG", 2: "RA_ERR_UNSUPPORTED", 3: "RA_
 EXPORTS = (
     "ra_block_attn_fwd", "ra_block_attn_fwd_merge", "ra_lse_merge", "ra_zigzag_shard_map",
     "ra_zigzag_gather", "ra_zigzag_scatter", "ra_cast_f32_bf16", "ra_rank_forward_workspace",
-    "ra_rank_forward", "ra_attn_bwd_delta", "ra_block_attn_bwd", "ra_rank_backward_workspace",
+    "ra_rank_forward", "ra_rank_forward_noalloc", "ra_attn_bwd_delta", "ra_block_attn_bwd", "ra_rank_backward_workspace",
     "ra_rank_backward", "ra_block_attn_work", "ra_forward_kernel", "ra_shard_tokens",
     "ra_step_segments", "ra_gather_tokens", "ra_scatter_tokens", "ra_block_attn_fwd_segments",
     "ra_segments_work", "ra_last_error", "ra_version",
@@ -110,6 +110,7 @@ def lib():
             "ra_cast_f32_bf16": [vp, vp, c_int64, vp],
             "ra_rank_forward_workspace": [POINTER(RankDesc), POINTER(c_size_t)],
             "ra_rank_forward": [POINTER(RankDesc), vp],
+            "ra_rank_forward_noalloc": [POINTER(RankDesc), vp],
             "ra_attn_bwd_delta": [vp, c_int, vp, c_int, c_int32, c_int32, c_int32, vp, vp],
             "ra_block_attn_bwd": [POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp],
             "ra_rank_backward_workspace": [POINTER(RankBwdDesc), POINTER(c_size_t)],
@@ -342,6 +343,15 @@ def ra_rank_forward_workspace(desc: RankDesc) -> int:
 
 def ra_rank_forward(desc: RankDesc, stream=None):
     _check(lib().ra_rank_forward(ctypes.byref(desc), _stream(stream)))
+
+
+RA_NOALLOC_SCRATCH_BYTES = 64 << 20   # include/ra.h
+
+
+def ra_rank_forward_noalloc(desc: RankDesc, stream=None):
+    """ra_rank_forward with the library's fixed scratch as workspace (the
+    descriptor's workspace fields are ignored)."""
+    _check(lib().ra_rank_forward_noalloc(ctypes.byref(desc), _stream(stream)))
 
 
 def ra_attn_bwd_delta(out, dout, delta, stream=None):

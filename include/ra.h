@@ -233,6 +233,25 @@ ra_status ra_rank_forward_workspace(const ra_rank_desc* d, size_t* bytes);
 ra_status ra_rank_forward(const ra_rank_desc* d, void* stream);
 
 /*
+ * ra_rank_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, kernels and results as ra_rank_forward, except that
+ * d->workspace and d->workspace_bytes are ignored: the workspace is a fixed
+ * array of RA_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU,
+ * held until the process ends (its device address is looked up once per
+ * device, on the first call with that device current).  The call allocates,
+ * frees and synchronises nothing.  A share whose ra_rank_forward_workspace
+ * size exceeds RA_NOALLOC_SCRATCH_BYTES is rejected with RA_ERR_INVALID_ARG
+ * before anything is queued.  Every call on one GPU uses that GPU's one
+ * array: calls whose queued work overlaps in time on the same GPU (other
+ * streams, other host threads) race on it and must be serialised by the
+ * caller.  Nothing in the array needs to start at zero: every byte a call
+ * reads was written earlier by the same call.
+ */
+#define RA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ra_status ra_rank_forward_noalloc(const ra_rank_desc* d, void* stream);
+
+/*
  * Backward, recomputing the probabilities from the saved final lse
  * (intelliparadigm section 4.3):
  *   delta_i = dout_i . out_i                      (ra_attn_bwd_delta)
