@@ -15,9 +15,15 @@ Default workload: 32K grouped-query causal attention (32 query heads over
 Prints one JSON line.  ``value`` is the effective attention TFLOP/s of the
 whole step (causal FLOPs counted once: 2*(dqk+dv) per visible pair per
 query head).  ``roofline`` is for the dominant kernel, the bf16 block
-attention forward: algorithmic FLOPs over its average launch duration, the
-durations taken with HIP events the library records on the launch stream
-around every attention launch of the timed steps.
+attention forward: algorithmic FLOPs over its average launch duration.  In
+the default fused form the timed steps consist of nothing but the C
+attention launches per step, back to back, so the average launch is the
+timed region (two HIP events on the launch stream) over the launch count.
+A second, untimed-for-``value`` pass of the same steps records HIP events
+around every launch (the library records them on the launch stream) for
+the per-launch and per-rank median / min / max in ``stats`` and
+``per_rank``; the per-block forms take their launch durations from such
+events directly.
 """
 from __future__ import annotations
 
@@ -64,6 +70,14 @@ def parse():
     ap.add_argument("--merge", type=int, default=0,
                     help="1: time ra_lse_merge alone on the workload's full-row step (every "
                          "local row, every query head, fp32 partials) and report HBM GB/s")
+    ap.add_argument("--mfma-ceiling", type=int, default=0,
+                    help="1: time a pure v_mfma_f32_32x32x16_bf16 loop on operands drawn like "
+                         "the workload's (and on constant ones): the matrix cores' sustained "
+                         "rate on this data")
+    ap.add_argument("--per-block-steps", type=int, default=5,
+                    help="after a fused (--fuse-merge 2) run, time this many steps with one "
+                         "launch per ring block to report diagonal vs history launches "
+                         "(0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB 3 times (the "
                          "reference kernel that scales HBM byte counters), then exit")
@@ -71,7 +85,14 @@ def parse():
 
 
 def bench_merge(a, w, torch, L):
-    """ra_lse_merge on one full-row step of a rank share: HBM-bound, in GB/s."""
+    """ra_lse_merge on one full-row step of a rank share: HBM-bound, in GB/s.
+
+    Cache-cold: the merge's working set (both partials and lses, ~203 MB for
+    the 32K workload) fits the 256 MB Infinity Cache, so a 1 GiB buffer is
+    read (summed) between merges and every merge is timed alone by HIP events
+    on the stream it runs on.  The buffer is read rather than written so that
+    no dirty cache lines are left to drain to HBM during the timed merge.
+    """
     import numpy as np
     dev = torch.device("cuda:0")
     T = w.seqlen // w.cp                        # local rows of a rank share
@@ -82,30 +103,111 @@ def bench_merge(a, w, torch, L):
     ob = torch.randn((T, w.hq, w.dv), generator=g, device=dev)
     la = torch.randn((w.hq, T), generator=g, device=dev)
     lb = torch.randn((w.hq, T), generator=g, device=dev)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)      # 1 GiB
+    stream = torch.cuda.current_stream()
     for _ in range(a.warmup):
         L.ra_lse_merge(oa, la, ob, lb, cud, cu, 0)
-    stream = torch.cuda.current_stream()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(a.steps)]
     torch.cuda.synchronize()
-    t0.record(stream)
-    for _ in range(a.steps):
+    for i in range(a.steps):
+        flush.sum()                             # reads 1 GiB: evicts the caches
+        ev[i][0].record(stream)
         L.ra_lse_merge(oa, la, ob, lb, cud, cu, 0)
-    t1.record(stream)
+        ev[i][1].record(stream)
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / a.steps
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    # the same stream shape without the merge arithmetic, as a practical
+    # ceiling of this read/read/write mix: torch's elementwise add of the two
+    # partials into a third buffer, cache-cold in the same way
+    oc = torch.empty_like(oa)
+    for _ in range(a.warmup):
+        torch.add(oa, ob, out=oc)
+    ev2 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    for i in range(a.steps):
+        flush.sum()
+        ev2[i][0].record(stream)
+        torch.add(oa, ob, out=oc)
+        ev2[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms_add = sorted(e0.elapsed_time(e1) for e0, e1 in ev2)
+    add_bytes = 3 * oa.numel() * 4
     nbytes = T * w.hq * (12 * w.dv + 12)       # read both partials and lses, write acc + lse
-    gbs = nbytes / (ms / 1e3) / 1e9
+    mean = sum(ms) / len(ms)
+    med = ms[len(ms) // 2]
+    gbs = nbytes / (mean / 1e3) / 1e9
     return {
-        "metric": "lse merge HBM GB/s (one full-row step of a rank share, fp32 partials), 1 GPU",
+        "metric": "lse merge HBM GB/s (one full-row step of a rank share, fp32 partials, "
+                  "cache-cold), 1 GPU",
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": a.steps,
-        "warmup": a.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "warmup": a.warmup, "ms_per_step": round(mean, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded N(0,1))",
-        "config": {"workload": f"{w.name}: ra_lse_merge of {T} rows x {w.hq} heads x dv {w.dv}",
+        "config": {"workload": f"{w.name}: ra_lse_merge of {T} rows x {w.hq} heads x dv {w.dv}, "
+                               f"1 GiB read between merges",
                    "bytes_per_merge": nbytes},
+        "stats": {"merge_ms_median": round(med, 5), "merge_ms_min": round(ms[0], 5),
+                  "merge_ms_max": round(ms[-1], 5),
+                  "gbs_median": round(nbytes / (med / 1e3) / 1e9, 1),
+                  "gbs_best": round(nbytes / (ms[0] / 1e3) / 1e9, 1),
+                  "reference_torch_add_gbs_median":
+                      round(add_bytes / (ms_add[len(ms_add) // 2] / 1e3) / 1e9, 1),
+                  "reference_torch_add_bytes": add_bytes},
         "roofline": {"bound": "hbm", "kernel": "lse_merge_kernel", "achieved": round(gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": None},
+        "cpu_baseline": None,
+    }
+
+
+def bench_mfma_ceiling(a, w, torch, L):
+    """Sustained v_mfma_f32_32x32x16_bf16 rate of a pure product loop (two
+    waves per SIMD, no memory traffic in the loop) on operands drawn like the
+    workload's inputs (its Q draw, bf16), and on constant operands: the rate
+    the attention kernels are bounded by on this data."""
+    import synth
+    dev = torch.device("cuda:0")
+    ops = synth.cast(w.q(0, 8192), w.dtype).to(dev).contiguous()     # 8192 tokens of Q
+    const = torch.full_like(ops, 0.25)
+    n_wg, iters = 512, 4000                                          # two workgroups per CU
+    out = torch.empty(n_wg * 256, dtype=torch.float32, device=dev)
+    flops = n_wg * 4 * iters * 64 * 2 * 32 * 32 * 16
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, buf in (("workload_operands", ops), ("constant_operands", const)):
+        for _ in range(2):
+            L.ra_mfma_ceiling(buf, out, n_wg, iters)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(a.steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in ev:
+            e0.record(stream)
+            L.ra_mfma_ceiling(buf, out, n_wg, iters)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+        med = ms[len(ms) // 2]
+        res[name] = {"ms_median": round(med, 4), "ms_min": round(ms[0], 4),
+                     "tflops_median": round(flops / (med / 1e3) / 1e12, 1),
+                     "tflops_best": round(flops / (ms[0] / 1e3) / 1e12, 1),
+                     "frac_median": round(flops / (med / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    v = res["workload_operands"]["tflops_median"]
+    return {
+        "metric": "MFMA-loop ceiling: sustained v_mfma_f32_32x32x16_bf16 TFLOP/s, 1 GPU",
+        "value": v, "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": 2,
+        "ms_per_step": res["workload_operands"]["ms_median"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": f"operands: the first 8192 tokens of the {w.name} Q draw (seeded "
+                f"N(0,1)*{w.mult:g}, bf16), or constant 0.25",
+        "config": {"workload": f"pure product loop, {n_wg} workgroups x 4 waves (two per SIMD), "
+                               f"{iters} x 64 products per wave, 8 accumulator chains",
+                   "flop_per_launch": flops},
+        "ceiling": res,
+        "roofline": {"bound": "mfma", "kernel": "mfma_ceiling_kernel", "achieved": v,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(v / PEAK_BF16_TFLOPS, 4), "traffic": None},
         "cpu_baseline": None,
     }
 
@@ -179,7 +281,32 @@ def cpu_baseline(w, budget_s: float):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"rank 0 of {w.name}: {done} of {len(rows)} local rows (random), all "
-                      f"{w.hq} query heads over every visible key, float64 NumPy, {dt:.1f} s"}
+                      f"{w.hq} query heads over every visible key, float64 NumPy, {dt:.1f} s",
+            "cpu_model": cpu_model(), "blas": blas_vendor()}
+
+
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def blas_vendor() -> str:
+    """BLAS library NumPy calls (name, version, threads), as threadpoolctl reports it."""
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                return (f"{i.get('internal_api')} {i.get('version')} "
+                        f"({i.get('threading_layer', '')}, {i.get('num_threads')} threads)")
+    except Exception:
+        pass
+    return "unknown"
 
 
 def bench_backward(a, w, prob, torch, L):
@@ -376,6 +503,107 @@ def bench_map(a, w, q, k, v, torch, L):
     }
 
 
+def _median(x):
+    x = sorted(x)
+    n = len(x)
+    return x[n // 2] if n % 2 else 0.5 * (x[n // 2 - 1] + x[n // 2])
+
+
+def launch_stats(ev, work, fl_pair, C, steps, fuse_merge):
+    """Median / min / max of the step span (first event of rank 0 to the last
+    of rank C-1: the step's launches back to back) and of the attention
+    launches, with the effective TFLOP/s they give."""
+    step_fl = sum(p for r in range(C) for (p, _, _) in work[r]) * fl_pair
+    last = 1 if fuse_merge == 2 else 2 * C - 1     # the fused form records events 0, 1 only
+    spans = [ev[i][0][0].elapsed_time(ev[i][C - 1][last]) for i in range(steps)]
+    launch = []                                   # (ms, flops) per attention launch
+    for i in range(steps):
+        for r in range(C):
+            if fuse_merge == 2:
+                launch.append((ev[i][r][0].elapsed_time(ev[i][r][1]),
+                               sum(p for (p, _, _) in work[r]) * fl_pair))
+            else:
+                for s in range(C):
+                    launch.append((ev[i][r][2 * s].elapsed_time(ev[i][r][2 * s + 1]),
+                                   work[r][s][0] * fl_pair))
+    tf = [f / (d / 1e3) / 1e12 for d, f in launch if d > 0]
+    ms = [d for d, _ in launch]
+    return {
+        "step_span_ms_median": round(_median(spans), 4),
+        "step_span_ms_min": round(min(spans), 4),
+        "step_span_ms_max": round(max(spans), 4),
+        "step_tflops_median": round(step_fl / (_median(spans) / 1e3) / 1e12, 2),
+        "step_tflops_best": round(step_fl / (min(spans) / 1e3) / 1e12, 2),
+        "launch_ms_median": round(_median(ms), 5),
+        "launch_ms_min": round(min(ms), 5),
+        "launch_ms_max": round(max(ms), 5),
+        "launch_tflops_median": round(_median(tf), 2),
+        "launch_tflops_best": round(max(tf), 2),
+        "launch_tflops_worst": round(min(tf), 2),
+    }
+
+
+def per_block_pass(a, w, prob, work, fl_pair, torch, L):
+    """The same step as one launch per ring block plus ra_lse_merge per history
+    block (fuse_merge = 0): effective TFLOP/s of the diagonal (causal) launches
+    and of the history (non-causal) launches, FLOP-weighted over all C^2
+    launches, after the headline's timed steps."""
+    C = w.cp
+    bufs = [prob.alloc_forward(torch.bfloat16, 0) for _ in range(C)]
+    stream = torch.cuda.current_stream()
+
+    def run(events=None):
+        for r in range(C):
+            out, lse, ws = bufs[r]
+            prob.forward(r, out, lse, ws, fuse_merge=0,
+                         events=None if events is None else events[r])
+
+    for _ in range(2):
+        run()
+    ev = []
+    for _ in range(a.per_block_steps):
+        e2 = []
+        for _ in range(C):
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * C)]
+            for e in evs:
+                e.record(stream)
+            e2.append(evs)
+        ev.append(e2)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(a.per_block_steps):
+        run(ev[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / a.per_block_steps
+    d_ms = h_ms = d_fl = h_fl = 0.0
+    for i in range(a.per_block_steps):
+        for r in range(C):
+            for s in range(C):
+                d = ev[i][r][2 * s].elapsed_time(ev[i][r][2 * s + 1])
+                f = work[r][s][0] * fl_pair
+                if s == 0:
+                    d_ms += d
+                    d_fl += f
+                else:
+                    h_ms += d
+                    h_fl += f
+    step_fl = sum(p for r in range(C) for (p, _, _) in work[r]) * fl_pair
+    names = {L.ra_forward_kernel(prob.step_desc(0, j, c, qp, kp), qp)
+             for (j, c, qp, kp) in prob.step_plan(0)}
+    del bufs
+    return {
+        "fuse_merge": 0, "steps": a.per_block_steps, "kernel": "/".join(sorted(names)),
+        "launches": a.per_block_steps * C * C,
+        "diag_tflops": round(d_fl / (d_ms / 1e3) / 1e12, 2) if d_ms else None,
+        "history_tflops": round(h_fl / (h_ms / 1e3) / 1e12, 2) if h_ms else None,
+        "all_launches_tflops": round((d_fl + h_fl) / ((d_ms + h_ms) / 1e3) / 1e12, 2),
+        "step_tflops": round(step_fl / (ms_step / 1e3) / 1e12, 2),
+        "ms_per_step": round(ms_step, 4),
+    }
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -400,6 +628,9 @@ def main():
     torch.cuda.set_device(dev)
     if a.merge:
         print(json.dumps(bench_merge(a, w, torch, L)), flush=True)
+        return
+    if a.mfma_ceiling:
+        print(json.dumps(bench_mfma_ceiling(a, w, torch, L)), flush=True)
         return
     print(f"# workload {w.name}: S={w.seqlen} CP={w.cp} hq={w.hq} hkv={w.hkv} "
           f"d={w.dqk}/{w.dv} {w.dtype}", file=sys.stderr, flush=True)
@@ -443,18 +674,24 @@ def main():
             prob.forward(r, out, lse, ws, fuse_merge=a.fuse_merge,
                          events=None if events is None else events[r])
 
+    # The per-launch events of the second pass are created first: creating
+    # and recording thousands of events idles the GPU for tens of ms, after
+    # which the clock takes ~20 launches to settle, and an event recorded
+    # between two launches leaves a ~10 us gap before the next one.  So the
+    # timed steps run right after the warmup, back to back, bracketed by two
+    # events only; every launch then starts as soon as the previous ends.
+    ev = [[make_events(2 * C) for _ in range(C)] for _ in range(a.steps)]
     for _ in range(a.warmup):
         run_step()
     torch.cuda.synchronize()
     print("# warmup done", file=sys.stderr, flush=True)
 
-    ev = [[make_events(2 * C) for _ in range(C)] for _ in range(a.steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     t_start.record(stream)
     for i in range(a.steps):
-        run_step(ev[i])
+        run_step()
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
@@ -463,7 +700,14 @@ def main():
     print(f"# timed {a.steps} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / a.steps:.3f})",
           file=sys.stderr, flush=True)
 
-    # per-launch attention durations
+    # second pass, same steps with events around every attention launch:
+    # per-launch and per-rank durations (median / min), diagonal vs history
+    for _ in range(2):
+        run_step()
+    torch.cuda.synchronize()
+    for i in range(a.steps):
+        run_step(ev[i])
+    torch.cuda.synchronize()
     attn_ms = 0.0
     attn_flops = 0.0
     diag_ms = hist_ms = 0.0
@@ -492,9 +736,21 @@ def main():
                 else:
                     hist_ms += d
                     hist_fl += f
-    achieved = attn_flops / (attn_ms / 1e3) / 1e12
-    avg_launch_ms = attn_ms / n_launch
     value = step_flops / (ms_step / 1e3) / 1e12
+    if a.fuse_merge == 2:
+        # the timed steps hold nothing but the C attention launches of each
+        # step, back to back: the average launch takes the timed region over
+        # the launch count (their dispatch gaps included)
+        avg_launch_ms = ms_total / (a.steps * C)
+        achieved = value
+        evented_launch_ms = attn_ms / n_launch
+    else:
+        # per-block steps also run merges and casts: per-launch events
+        avg_launch_ms = attn_ms / n_launch
+        achieved = attn_flops / (attn_ms / 1e3) / 1e12
+        evented_launch_ms = avg_launch_ms
+    stats = launch_stats(ev, work, fl_pair, C, a.steps, a.fuse_merge)
+    stats["evented_launch_ms_mean"] = round(evented_launch_ms, 5)
     if a.fuse_merge == 2:
         kname = L.ra_forward_kernel(prob.local_desc(0), L.PART_ALL)
     else:
@@ -534,10 +790,11 @@ def main():
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "avg_launch_ms": round(avg_launch_ms, 5),
-            "launches": n_launch,
+            "launches": a.steps * C if a.fuse_merge == 2 else n_launch,
             "diag_tflops": round(diag_fl / (diag_ms / 1e3) / 1e12, 2) if diag_ms else None,
             "history_tflops": round(hist_fl / (hist_ms / 1e3) / 1e12, 2) if hist_ms else None,
         },
+        "stats": stats,
         "per_rank": {
             "ms": [round(x, 4) for x in rank_ms],
             "pairs_x_heads": [int(sum(p for (p, _, _) in work[r])) for r in range(C)],
@@ -550,7 +807,11 @@ def main():
         },
         "cpu_baseline": None,
     }
-    del bufs, prob
+    del bufs
+    torch.cuda.empty_cache()
+    if a.fuse_merge == 2 and a.per_block_steps > 0:
+        res["per_block"] = per_block_pass(a, w, prob, work, fl_pair, torch, L)
+    del prob
     torch.cuda.empty_cache()
     if a.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)

@@ -30,7 +30,7 @@ EXPORTS = (
     "ra_rank_forward", "ra_rank_forward_noalloc", "ra_attn_bwd_delta", "ra_block_attn_bwd", "ra_rank_backward_workspace",
     "ra_rank_backward", "ra_block_attn_work", "ra_forward_kernel", "ra_shard_tokens",
     "ra_step_segments", "ra_gather_tokens", "ra_scatter_tokens", "ra_block_attn_fwd_segments",
-    "ra_segments_work", "ra_last_error", "ra_version",
+    "ra_segments_work", "ra_mfma_ceiling", "ra_last_error", "ra_version",
 )
 
 # ra_map values by name (the oracle's names for the same placements)
@@ -125,6 +125,7 @@ def lib():
                                            vp],
             "ra_segments_work": [vp, c_int32, c_int32, POINTER(c_int64), POINTER(c_int64),
                                  POINTER(c_int64)],
+            "ra_mfma_ceiling": [vp, c_int64, vp, c_int64, c_int32, c_int32, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -448,6 +449,13 @@ def ra_forward_kernel(desc: AttnDesc, q_part: int = PART_ALL) -> str:
     if r is None:
         raise RaError(1, lib().ra_last_error().decode())
     return r.decode()
+
+
+def ra_mfma_ceiling(operands, out, n_workgroups: int, iters: int, stream=None):
+    """Pure v_mfma_f32_32x32x16_bf16 loop on the given bf16 operands (a
+    measurement helper); out holds n_workgroups x 256 floats."""
+    _check(lib().ra_mfma_ceiling(_ptr(operands), operands.numel() * operands.element_size(),
+                                 _ptr(out), out.numel(), n_workgroups, iters, _stream(stream)))
 
 
 def ra_last_error() -> str:

@@ -412,6 +412,20 @@ ra_status ra_segments_work(const ra_segment* segs, int32_t n_seg, int32_t hq,
  */
 const char* ra_forward_kernel(const ra_attn_desc* d, ra_part q_part);
 
+/*
+ * Measurement helper (not part of the attention path): n_workgroups x 4
+ * waves each run iters x 64 products v_mfma_f32_32x32x16_bf16 (8
+ * independent accumulator chains, 32768 FLOP per product) on bf16 operand
+ * fragments read once from `operands` (device, operand_bytes >= 16 KiB, a
+ * multiple of 16, 16-byte aligned; read with wrap-around), and write one
+ * float per lane to `out` (device, out_floats >= n_workgroups x 256, else
+ * RA_ERR_INVALID_ARG before any launch).  Timed by
+ * the caller, it gives the rate the matrix cores sustain on operands of a
+ * given distribution, which bounds the attention kernels on that data.
+ */
+ra_status ra_mfma_ceiling(const void* operands, int64_t operand_bytes, float* out,
+                          int64_t out_floats, int32_t n_workgroups, int32_t iters, void* stream);
+
 /* Thread-local description of the last non-OK status ("" if none). */
 const char* ra_last_error(void);
 

@@ -489,3 +489,13 @@ def test_segment_launch_validation():
     tok = np.array([0, 5], np.int32)
     assert L.lib().ra_gather_tokens(FAKE, FAKE, 256, 5, FAKE, tok.ctypes.data, 2,
                                     None) == L.RA_ERR_INVALID_ARG          # token 5 >= 5 rows
+
+
+def test_mfma_ceiling_validation():
+    """The measurement helper rejects short buffers before any launch."""
+    lib = L.lib()
+    assert lib.ra_mfma_ceiling(FAKE, 1 << 16, FAKE, 255, 1, 1, None) == L.RA_ERR_INVALID_ARG
+    assert "floats" in L.ra_last_error()
+    assert lib.ra_mfma_ceiling(FAKE, 1024, FAKE, 256, 1, 1, None) == L.RA_ERR_INVALID_ARG
+    assert lib.ra_mfma_ceiling(None, 1 << 16, FAKE, 256, 1, 1, None) == L.RA_ERR_INVALID_ARG
+    assert lib.ra_mfma_ceiling(FAKE, 1 << 16, FAKE, 256, 1, 0, None) == L.RA_ERR_INVALID_ARG
