@@ -67,6 +67,10 @@ def parse():
     ap.add_argument("--backward", type=int, default=0,
                     help="1: time the backward shares (after one forward) instead; for the "
                          "256K MLA workload")
+    ap.add_argument("--bwd-rank-fused", type=int, default=-1,
+                    help="backward: 1 = one dK/dV and one dQ launch per rank share (every owner's "
+                         "blocks), 0 = one pair of launches per ring step, -1 = the library's "
+                         "choice (fused for packed documents and small shares)")
     ap.add_argument("--merge", type=int, default=0,
                     help="1: time ra_lse_merge alone on the workload's full-row step (every "
                          "local row, every query head, fp32 partials) and report HBM GB/s")
@@ -310,9 +314,16 @@ def blas_vendor() -> str:
 
 
 def bench_backward(a, w, prob, torch, L):
-    """Backward step: every rank's ra_rank_backward (delta, then dQ and dK/dV per block)."""
+    """Backward step: every rank's ra_rank_backward (delta, then dK/dV over
+    every owner's key tiles and dQ over all blocks in one launch each, or
+    with --bwd-rank-fused 0 one dQ and one dK/dV launch per ring step)."""
     import synth
     C = w.cp
+    if a.bwd_rank_fused in (0, 1):
+        os.environ["RA_BWD_RANK_FUSED"] = str(a.bwd_rank_fused)
+    else:
+        os.environ.pop("RA_BWD_RANK_FUSED", None)
+    form = {0: "per ring step", 1: "rank-fused"}.get(a.bwd_rank_fused, "library's choice")
     dev = prob.q[0].device
     do = synth.cast(w.do(), w.dtype).to(dev)
     prob.do = [prob.gather(do, r) for r in range(C)]
@@ -356,8 +367,10 @@ def bench_backward(a, w, prob, torch, L):
     t1.record(stream)
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / a.steps
-    blk_ms = sum(ev[i][r][2 * s].elapsed_time(ev[i][r][2 * s + 1])
-                 for i in range(a.steps) for r in range(C) for s in range(C))
+    # both forms record event 0 before a rank's first launch and event 2C-1
+    # after its last: the rank's span
+    blk_ms = sum(ev[i][r][0].elapsed_time(ev[i][r][2 * C - 1])
+                 for i in range(a.steps) for r in range(C))
     achieved = step_flops * a.steps / (blk_ms / 1e3) / 1e12
     res = {
         "metric": "effective attention backward TFLOP/s per rank-share (bf16), 1 GPU",
@@ -370,7 +383,8 @@ def bench_backward(a, w, prob, torch, L):
                                f"head dim {w.dqk}/{w.dv}",
                    "step_effective_tflop": round(step_flops / 1e12, 4),
                    "flop_per_pair": fl_pair},
-        "roofline": {"bound": "mfma", "kernel": "attn_bwd_dq + attn_bwd_dkdv",
+        "roofline": {"bound": "mfma",
+                     "kernel": f"attn_bwd_dq + attn_bwd_dkdv ({form})",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": None},

@@ -251,21 +251,11 @@ struct Step {
 Step plan_step(int rank, int s, int cp) {
   Step p;
   p.owner = ((rank - s) % cp + cp) % cp;
-  if (s == 0) {
-    p.causal = 1;
-    p.q_part = RA_PART_ALL;
-    p.k_part = RA_PART_ALL;
-  } else if (p.owner < rank) {
-    // the owner's first chunk precedes both of ours, its second follows both
-    p.causal = 0;
-    p.q_part = RA_PART_ALL;
-    p.k_part = RA_PART_FIRST_HALF;
-  } else {
-    // both owner chunks lie between our first and our second chunk
-    p.causal = 0;
-    p.q_part = RA_PART_SECOND_HALF;
-    p.k_part = RA_PART_ALL;
-  }
+  int causal, q_part, k_part;
+  ra::owner_plan(rank, p.owner, &causal, &q_part, &k_part);
+  p.causal = causal;
+  p.q_part = (ra_part)q_part;
+  p.k_part = (ra_part)k_part;
   return p;
 }
 
@@ -938,15 +928,52 @@ static ra_status rank_bwd_step(const ra_rank_bwd_desc* d, int s, ra_attn_desc* s
   return check_desc(sd, true, cs);
 }
 
-// Workspace: delta [hq, total_q], then the dK/dV partials of query shares
-// 1 .. qsplit-1 of the step kind that splits most.  Every kind a rank of
-// the ring can meet is counted (the diagonal block, an earlier and a later
-// owner's block), so one workspace serves every rank.
+// Rank-fused backward: one dK/dV launch over every owner's key tiles and
+// one dQ launch whose query tiles walk all owners' blocks, instead of one
+// pair of launches per ring step.  It pays where the per-step launches are
+// small or cut into many documents: packed documents, or shares of at most
+// 64K (row, head) pairs (8K MHA 206 -> 231, 128K varlen 128 -> 148 TFLOP/s
+// on one box).  Large single-sequence shares keep the per-step launches,
+// whose workgroups stream the same Q/dO (or K/V) tiles in step through the
+// L2 (32K GQA 483 vs 382, 256K MLA 569 vs 438 fused).
+// RA_BWD_RANK_FUSED=0 / =1 in the environment forces one form.
+static bool bwd_rank_fused(const ra_attn_desc& L, const Checked& c) {
+  const char* e = std::getenv("RA_BWD_RANK_FUSED");
+  if (e && !std::strcmp(e, "0")) return false;
+  if (e && !std::strcmp(e, "1")) return true;
+  return L.n_seq > 1 || (long long)c.total_q * L.hq <= 65536;
+}
+
+// dQ key split of the rank-fused backward: the walk's key tiles of a query
+// tile dealt over up to kMaxQsplit workgroups, doubled until the launch has
+// 256 workgroups (the dK/dV launch over all owners is large enough alone).
+// RA_BWD_KSPLIT=n in the environment forces n.
+static int bwd_rank_ksplit(const ra_attn_desc& L, const Checked& c) {
+  const char* e = std::getenv("RA_BWD_KSPLIT");
+  if (e && *e) return std::max(1, std::min(std::atoi(e), kMaxQsplit));
+  const long long wg = (long long)L.n_seq * L.hq * ((c.max_q_part + 127) / 128);
+  int n = 1;
+  while (n < kMaxQsplit && wg * n < 256) n *= 2;
+  return n;
+}
+
+// Workspace: delta [hq, total_q], then
+//  - rank-fused: the dQ partials of key shares 1 .. ksplit-1;
+//  - per step: the dK/dV partials of query shares 1 .. qsplit-1 (and dQ
+//    partials) of the step kind that splits most.  Every kind a rank of the
+//    ring can meet is counted (the diagonal block, an earlier and a later
+//    owner's block), so one workspace serves every rank.
 ra_status ra_rank_backward_workspace(const ra_rank_bwd_desc* d, size_t* bytes) {
   if (!d || !bytes) return fail(RA_ERR_INVALID_ARG, "NULL argument");
   Checked c;
   ra_status st = check_rank_common(d->local, d->cp_size, d->rank, d->k_blocks, d->v_blocks, &c);
   if (st != RA_OK) return st;
+  const size_t delta_b = align256((size_t)c.total_q * d->local.hq * sizeof(float));
+  if (bwd_rank_fused(d->local, c)) {
+    const size_t part = align256((size_t)c.total_q * d->local.hq * d->local.dqk * sizeof(float));
+    *bytes = delta_b + (size_t)(bwd_rank_ksplit(d->local, c) - 1) * part;
+    return ok();
+  }
   size_t parts = 0;
   const int n_kinds = d->cp_size > 1 ? 3 : 1;
   for (int kind = 0; kind < n_kinds; ++kind) {
@@ -964,7 +991,7 @@ ra_status ra_rank_backward_workspace(const ra_rank_bwd_desc* d, size_t* bytes) {
     if ((st = check_desc(&sd, true, &cs)) != RA_OK) return st;
     parts = std::max(parts, bwd_step_parts(&sd, cs));
   }
-  *bytes = align256((size_t)c.total_q * d->local.hq * sizeof(float)) + parts;
+  *bytes = delta_b + parts;
   return ok();
 }
 
@@ -998,8 +1025,61 @@ ra_status ra_rank_backward(const ra_rank_bwd_desc* d, void* stream) {
   float* delta = static_cast<float*>(d->workspace);
   const size_t delta_b = align256((size_t)c.total_q * L.hq * sizeof(float));
   float* part = reinterpret_cast<float*>(static_cast<char*>(d->workspace) + delta_b);
-  hipError_t e = ra::launch_bwd_delta(d->out, d->out_dtype, d->dout, L.dtype, c.total_q, L.hq,
-                                      L.dv, delta, hs);
+  hipError_t e;
+  if (bwd_rank_fused(L, c)) {
+    if (d->cp_size > ra::kMaxCp)
+      return fail(RA_ERR_UNSUPPORTED, "rank-fused backward supports cp_size <= %d", ra::kMaxCp);
+    ra::RankKV rk;
+    ra::RankGrad rg;
+    std::memset(&rk, 0, sizeof(rk));
+    std::memset(&rg, 0, sizeof(rg));
+    rk.cp = d->cp_size;
+    rk.rank = d->rank;
+    for (int j = 0; j < d->cp_size; ++j) {
+      rk.k[j] = d->k_blocks[j];
+      rk.v[j] = d->v_blocks[j];
+      rg.dk[j] = d->dk_blocks[j];
+      rg.dv[j] = d->dv_blocks[j];
+    }
+    ra_attn_desc sd = L;
+    sd.k = d->k_blocks[0];
+    sd.v = d->v_blocks[0];
+    sd.causal = 0;
+    sd.q_part = RA_PART_ALL;
+    sd.k_part = RA_PART_ALL;
+    Checked cs;
+    if ((st = check_desc(&sd, true, &cs)) != RA_OK) return st;
+    ra::AttnArgs a = make_args(&sd, cs);
+    a.n_ktiles = (cs.max_k_part + 127) / 128;
+    a.dout = d->dout;
+    a.lse_in = d->lse;
+    a.delta = delta;
+    a.dq = d->dq;
+    const int ksplit = bwd_rank_ksplit(L, c);
+    a.ksplit = ksplit;
+    a.dq_part = ksplit > 1 ? part : nullptr;
+    if (d->events && d->events[0] &&
+        (e = hipEventRecord((hipEvent_t)d->events[0], hs)) != hipSuccess)
+      return hip_fail(e, "event record");
+    e = ra::launch_bwd_delta(d->out, d->out_dtype, d->dout, L.dtype, c.total_q, L.hq, L.dv,
+                             delta, hs);
+    if (e != hipSuccess) return hip_fail(e, "delta launch");
+    if (a.n_qtiles > 0) {
+      e = ra::launch_rank_bwd_bf16(a, rk, rg, L.dqk, L.dv, hs);
+      if (e == hipErrorInvalidValue) return fail(RA_ERR_UNSUPPORTED, "backward variant not built");
+      if (e != hipSuccess) return hip_fail(e, "rank backward launch");
+    }
+    void* last = d->events ? d->events[2 * d->cp_size - 1] : nullptr;
+    if (last && (e = hipEventRecord((hipEvent_t)last, hs)) != hipSuccess)
+      return hip_fail(e, "event record");
+    return ok();
+  }
+  // events[0] goes before delta, so that it marks the rank's first launch
+  if (d->events && d->events[0] &&
+      (e = hipEventRecord((hipEvent_t)d->events[0], hs)) != hipSuccess)
+    return hip_fail(e, "event record");
+  e = ra::launch_bwd_delta(d->out, d->out_dtype, d->dout, L.dtype, c.total_q, L.hq, L.dv, delta,
+                           hs);
   if (e != hipSuccess) return hip_fail(e, "delta launch");
   for (int s = 0; s < d->cp_size; ++s) {
     ra_attn_desc sd;
@@ -1012,7 +1092,7 @@ ra_status ra_rank_backward(const ra_rank_bwd_desc* d, void* stream) {
       return fail(RA_ERR_INVALID_ARG, "workspace too small for the dK/dV and dQ splits");
     float* dq_part = reinterpret_cast<float*>(reinterpret_cast<char*>(part) +
                                               (size_t)(qsplit - 1) * bwd_part_bytes(&sd, cs));
-    if (d->events && d->events[2 * s] &&
+    if (s > 0 && d->events && d->events[2 * s] &&
         (e = hipEventRecord((hipEvent_t)d->events[2 * s], hs)) != hipSuccess)
       return hip_fail(e, "event record");
     st = launch_bwd(&sd, cs, d->dout, d->lse, delta, d->dq, d->dk_blocks[owner],

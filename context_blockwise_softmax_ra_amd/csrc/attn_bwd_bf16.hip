@@ -39,6 +39,8 @@
 // the LDS operand reads of a block of products are scheduled a few products
 // ahead (pipeline_lds_mfma).
 
+#include <cstring>
+
 #include "mfma_common.h"
 
 namespace ra {
@@ -85,8 +87,12 @@ struct GeoKV {
 // a fixed order (wave 0 + 1 + 2 + 3) through LDS at the end, so the result
 // stays deterministic.  It gives 4x the workgroups of the 128-key form, for
 // launches with few key tiles (GQA/MHA history blocks at d_qk = 128).
-template <int DQK, int DV, bool CAUSAL, bool QS>
-__global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
+// RANK: a rank's whole backward share in one launch; the slowest index of
+// the grid is the ring step o (owner (rank - o) mod C, the diagonal block
+// first), and every workgroup takes its owner's K/V, dK/dV accumulators,
+// parts and causal rule (owner_plan); CAUSAL is then ignored.
+template <int DQK, int DV, bool CAUSAL, bool QS, bool RANK = false>
+__global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a, RankKV rk, RankGrad rg) {
   using G = GeoKV<DQK, DV>;
   constexpr int KBN = QS ? 32 : KV_BN;  // keys per workgroup
   constexpr int NS = QS ? NT / 64 : 1;  // stage sets (one per wave with QS)
@@ -101,21 +107,43 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
   // V of the workgroup's keys (dual layout): read as B operands of dP
   __shared__ __attribute__((aligned(1024))) char vsm[KBN * G::OROWB];
 
-  const int nsp = QS ? 1 : a.qsplit;  // workgroups sharing a key tile
-  // packed documents: deal key tiles (with their query shares) over the
-  // XCDs, since one document's tiles follow another's in logical order;
-  // otherwise contiguous ranges per XCD (neighbours share K/V in L2)
-  int b = a.n_seq > 1 ? xcd_deal(blockIdx.x, gridDim.x, nsp) : xcd_remap(blockIdx.x, gridDim.x);
+  const int nsp = QS || RANK ? 1 : a.qsplit;  // workgroups sharing a key tile
+  // One block: packed documents deal key tiles (with their query shares)
+  // over the XCDs, since one document's tiles follow another's in logical
+  // order; otherwise contiguous ranges per XCD (neighbours share K/V in L2).
+  // A rank share: the kv head is the slowest index and every XCD takes a
+  // contiguous range, i.e. the key tiles of one kv head over all owners and
+  // documents: they all read that head's Q and dO tiles, which then stay in
+  // the XCD's L2 (dealt over the XCDs, every L2 fetched every head's tiles;
+  // 32K GQA backward 478 -> 284 TFLOP/s).  The diagonal block comes first.
+  int b = (!RANK && a.n_seq > 1) ? xcd_deal(blockIdx.x, gridDim.x, nsp)
+                                 : xcd_remap(blockIdx.x, gridDim.x);
   const int sp = b % nsp;
   b /= nsp;
   const int kt = b % a.n_ktiles;
   b /= a.n_ktiles;
-  const int kvh = b % a.hkv;
-  const int seg = b / a.hkv;
+  int kvh, seg, step_o = 0;
+  if (RANK) {
+    seg = b % a.n_seq;
+    b /= a.n_seq;
+    step_o = b % rk.cp;
+    kvh = b / rk.cp;
+  } else {
+    kvh = b % a.hkv;
+    seg = b / a.hkv;
+  }
+  const int owner = RANK ? (rk.rank - step_o + rk.cp) % rk.cp : 0;
+  int own_causal = CAUSAL ? 1 : 0, own_qp = a.q_part, own_kp = a.k_part;
+  if (RANK) owner_plan(rk.rank, owner, &own_causal, &own_qp, &own_kp);
+  const bool causal = RANK ? own_causal != 0 : CAUSAL;
+  const void* kptr = RANK ? rk.k[owner] : a.k;
+  const void* vptr = RANK ? rk.v[owner] : a.v;
+  float* dkptr = RANK ? rg.dk[owner] : a.dk;
+  float* dvptr = RANK ? rg.dv[owner] : a.dv;
 
   int q_lo, q_hi, k_lo, k_hi;
-  part_range(a.cu_q[seg], a.cu_q[seg + 1], a.q_part, &q_lo, &q_hi);
-  part_range(a.cu_k[seg], a.cu_k[seg + 1], a.k_part, &k_lo, &k_hi);
+  part_range(a.cu_q[seg], a.cu_q[seg + 1], own_qp, &q_lo, &q_hi);
+  part_range(a.cu_k[seg], a.cu_k[seg + 1], own_kp, &k_lo, &k_hi);
   const int k0 = k_lo + kt * KBN;
   const int qlen = q_hi - q_lo, klen = k_hi - k_lo;
   if (k0 >= k_hi || qlen <= 0) return;
@@ -132,14 +160,14 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
   // workgroup's keys goes to LDS (keys past the block re-read the last one)
   bf16x8 kf[G::KK];
   {
-    const __bf16* kp = reinterpret_cast<const __bf16*>(a.k) + (int64_t)my_key * a.k_stride +
+    const __bf16* kp = reinterpret_cast<const __bf16*>(kptr) + (int64_t)my_key * a.k_stride +
                        (int64_t)kvh * DQK + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < G::KK; ++kk) kf[kk] = as_bf16x8(ldg16(kp + 16 * kk));
     DualLoader<KBN, DV, G::OROWB, NT / 64> lvk;
     const int64_t vsb = a.v_stride * 2;
     lvk.init(vsb, wave, lane);
-    lvk.issue(reinterpret_cast<const char*>(a.v) + ((int64_t)k0 * a.v_stride + (int64_t)kvh * DV) * 2,
+    lvk.issue(reinterpret_cast<const char*>(vptr) + ((int64_t)k0 * a.v_stride + (int64_t)kvh * DV) * 2,
               vsb, k_hi - k0, vsm);
   }
   const int vrow = (QS ? 0 : wave * 32) + l32;  // this lane's key row in vsm
@@ -150,7 +178,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
   for (int t = 0; t < G::NVT; ++t) dv[t] = zero16();
 
   const int n_qt = (qlen + KV_BQ - 1) / KV_BQ;
-  const int qt_begin = CAUSAL ? (kt * KBN) / KV_BQ : 0;
+  const int qt_begin = causal ? (kt * KBN) / KV_BQ : 0;
   const int per_head = n_qt - qt_begin;
   const int n_all = per_head > 0 ? per_head * a.group : 0;
   // this workgroup's share of the iterations: [it_lo, n_it)
@@ -188,7 +216,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
   auto tile = [&](int it, const char* qs, const char* os, const float* lsd)
       __attribute__((always_inline)) {
     const int qt_rel = (qt_begin + it % per_head) * KV_BQ;  // first query row (part-relative)
-    const bool live = wave_live && (!CAUSAL || qt_rel + KV_BQ - 1 >= wk_rel);
+    const bool live = wave_live && (!causal || qt_rel + KV_BQ - 1 >= wk_rel);
     if (!live) return;
     // S = Q K^T and dP = dO V^T, lane = key column, entry i = query row
     // 16*(i/8) + 8g + i%8 of the tile
@@ -203,7 +231,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
     pipeline_lds_mfma_n<G::KK, 1, G::VK, 2, kBwdAhead>();
     __builtin_amdgcn_sched_barrier(0);
     const bool need_mask = (my_key_rel >= klen) || (wk_rel + 31 >= klen) ||
-                           (CAUSAL && qt_rel < wk_rel + 31) || (qt_rel + KV_BQ > qlen);
+                           (causal && qt_rel < wk_rel + 31) || (qt_rel + KV_BQ > qlen);
     // A row that sees nothing (lse = -inf) only occurs in a masked tile:
     // every pair of an unmasked tile is visible.  Its exp overflows to inf
     // and the mask then replaces P by 0, so lse needs no guard.
@@ -215,7 +243,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
       float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -l2));
       if (need_mask) {
         const bool ok = (my_key_rel < klen) && (qt_rel + r < qlen) &&
-                        (!CAUSAL || my_key_rel <= qt_rel + r);
+                        (!causal || my_key_rel <= qt_rel + r);
         p = ok ? p : 0.f;
       }
       s[i] = p;
@@ -324,8 +352,8 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
       const int kr = wk_rel + 8 * (i >> 2) + 4 * g + (i & 3);
       if (kr >= klen) continue;
       const int64_t key = k_lo + kr;
-      float* dkp = a.dk + (key * a.hkv + kvh) * DQK + l32;
-      float* dvp = a.dv + (key * a.hkv + kvh) * DV + l32;
+      float* dkp = dkptr + (key * a.hkv + kvh) * DQK + l32;
+      float* dvp = dvptr + (key * a.hkv + kvh) * DV + l32;
 #pragma unroll
       for (int nt = 0; nt < G::NQT; ++nt) dkp[32 * nt] += scale * dk[nt][i];
 #pragma unroll
@@ -407,8 +435,21 @@ struct GeoQ {
   static_assert(DV == 128, "V rows are 256 bytes");
 };
 
-template <int DQK, int DV, bool CAUSAL>
-__global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a) {
+// How a KV block meets the query rows of a dQ workgroup (as in the forward).
+enum QKind {
+  QK_CAUSAL = 0,     // key j visible to row i iff j <= i (part-relative)
+  QK_ALL = 1,        // every key visible
+  QK_LATE_ROWS = 2,  // every key visible to the segment's second-half rows only
+};
+
+// RANK: a rank's whole backward share; every query tile walks the key tiles
+// of all C owners' blocks in ring order (the diagonal block first) with dQ
+// in registers, each block with its owner's K/V and rule (owner_plan).
+// Otherwise one block as described by the AttnArgs parts and CAUSAL.  With
+// a.ksplit > 1 the tiles of the walk are dealt round-robin over that many
+// workgroups of the same query tile.
+template <int DQK, int DV, bool CAUSAL, bool RANK = false>
+__global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a, RankKV rk) {
   using G = GeoQ<DQK, DV>;
   __shared__ __attribute__((aligned(1024))) char ks0[G::K_BYTES];
   __shared__ __attribute__((aligned(1024))) char ks1[G::K_BYTES];
@@ -417,29 +458,36 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a) {
   // dO of the workgroup's 128 query rows (dual layout): B operands of dP^T
   __shared__ __attribute__((aligned(1024))) char osm[Q_BM * G::VROWB];
 
-  // packed documents: deal query tiles (a kv group's heads and their key
-  // shares together) over the XCDs; otherwise contiguous ranges per XCD
+  // One block of packed documents: deal query tiles (a kv group's heads and
+  // their key shares together) over the XCDs; otherwise contiguous ranges
+  // per XCD.  A rank share: the kv head is the slowest index, so an XCD's
+  // contiguous range is one kv head's query tiles over all documents, which
+  // all walk that head's K/V tiles of every block (kept in the XCD's L2).
   const int nks = max(a.ksplit, 1);  // workgroups sharing a query tile
-  int b = a.n_seq > 1 ? xcd_deal(blockIdx.x, gridDim.x, a.group * nks)
-                      : xcd_remap(blockIdx.x, gridDim.x);
-  const int kshare = b % nks;  // this workgroup takes key tiles kshare, kshare + nks, ...
+  int b = (!RANK && a.n_seq > 1) ? xcd_deal(blockIdx.x, gridDim.x, a.group * nks)
+                                 : xcd_remap(blockIdx.x, gridDim.x);
+  const int kshare = b % nks;  // this workgroup takes tiles kshare, kshare + nks, ... of the walk
   b /= nks;
   const int hg = b % a.group;
   b /= a.group;
   const int qt_rev = b % a.n_qtiles;
   b /= a.n_qtiles;
-  const int kvh = b % a.hkv;
-  const int seg = b / a.hkv;
-  const int qt = CAUSAL ? (a.n_qtiles - 1 - qt_rev) : qt_rev;
+  int kvh, seg;
+  if (RANK) {
+    seg = b % a.n_seq;
+    kvh = b / a.n_seq;
+  } else {
+    kvh = b % a.hkv;
+    seg = b / a.hkv;
+  }
+  const int qt = (CAUSAL || RANK) ? (a.n_qtiles - 1 - qt_rev) : qt_rev;  // heaviest first
   const int h = kvh * a.group + hg;
 
-  int q_lo, q_hi, k_lo, k_hi;
-  part_range(a.cu_q[seg], a.cu_q[seg + 1], a.q_part, &q_lo, &q_hi);
-  part_range(a.cu_k[seg], a.cu_k[seg + 1], a.k_part, &k_lo, &k_hi);
+  int q_lo, q_hi;
+  part_range(a.cu_q[seg], a.cu_q[seg + 1], RANK ? RA_PART_ALL : a.q_part, &q_lo, &q_hi);
   const int q0 = q_lo + qt * Q_BM;
   if (q0 >= q_hi) return;
-  const int klen = k_hi - k_lo;
-  if (klen <= 0) return;  // nothing to add
+  const int qhalf = (q_hi - q_lo) >> 1;
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
@@ -451,9 +499,69 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a) {
   const int wq_first_rel = wq0 - q_lo;
   const int wq_last_rel = min(wq0 + 32, q_hi) - 1 - q_lo;
   const int qrel_last_wg = min(q0 + Q_BM, q_hi) - 1 - q_lo;
-  const int kend = CAUSAL ? min(klen, qrel_last_wg + 1) : klen;
-  const int wave_kend = CAUSAL ? min(klen, wq_last_rel + 1) : klen;
-  const int ntiles = (kend + Q_BN - 1) / Q_BN;
+  const int64_t ksb = a.k_stride * 2, vsb = a.v_stride * 2;
+  const int kseg0 = a.cu_k[seg], kseg1 = a.cu_k[seg + 1];
+  const int nblocks = RANK ? rk.cp : 1;
+
+  struct QBlock {
+    const char* kb;
+    const char* vb;
+    int klen, kind, ntiles;
+  };
+  auto get_block = [&](int bi) -> QBlock {
+    QBlock blk;
+    const void* kp;
+    const void* vp;
+    int kpart;
+    if (RANK) {
+      const int owner = (rk.rank - bi + rk.cp) % rk.cp;
+      kp = rk.k[owner];
+      vp = rk.v[owner];
+      blk.kind = bi == 0 ? QK_CAUSAL : (owner < rk.rank ? QK_ALL : QK_LATE_ROWS);
+      kpart = (bi != 0 && owner < rk.rank) ? RA_PART_FIRST_HALF : RA_PART_ALL;
+    } else {
+      kp = a.k;
+      vp = a.v;
+      blk.kind = CAUSAL ? QK_CAUSAL : QK_ALL;
+      kpart = a.k_part;
+    }
+    int k_lo, k_hi;
+    part_range(kseg0, kseg1, kpart, &k_lo, &k_hi);
+    blk.klen = k_hi - k_lo;
+    blk.kb = reinterpret_cast<const char*>(kp) + ((int64_t)k_lo * a.k_stride + (int64_t)kvh * DQK) * 2;
+    blk.vb = reinterpret_cast<const char*>(vp) + ((int64_t)k_lo * a.v_stride + (int64_t)kvh * DV) * 2;
+    int kend = blk.klen;
+    if (blk.kind == QK_CAUSAL) kend = min(blk.klen, qrel_last_wg + 1);
+    if (blk.kind == QK_LATE_ROWS && qrel_last_wg < qhalf) kend = 0;
+    blk.ntiles = kend > 0 ? (kend + Q_BN - 1) / Q_BN : 0;
+    return blk;
+  };
+  struct Cursor {
+    int bi, t;
+    QBlock blk;
+  };
+  // step a cursor by n tiles of the walk (past the end it stays put)
+  auto advance = [&](Cursor& c, int n) {
+    for (int i = 0; i < n; ++i) {
+      if (++c.t < c.blk.ntiles) continue;
+      c.t = 0;
+      do {
+        if (++c.bi >= nblocks) return;
+        c.blk = get_block(c.bi);
+      } while (c.blk.ntiles == 0);
+    }
+  };
+  int total = 0;
+  for (int bi = 0; bi < nblocks; ++bi) total += get_block(bi).ntiles;
+  if (total == 0) return;  // whole workgroup: nothing to add
+  Cursor cc;               // tile to compute
+  cc.bi = 0;
+  cc.t = 0;
+  cc.blk = get_block(0);
+  while (cc.blk.ntiles == 0 && cc.bi + 1 < nblocks) cc.blk = get_block(++cc.bi);
+  cc.t = -1;
+  advance(cc, kshare + 1);
+  Cursor lc = cc;          // tile to load
 
   const int row = min(my_row, q_hi - 1);
   // Q of this lane's row as B operands (k = dims 16kk + 8g .. +7); dO of the
@@ -480,25 +588,34 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a) {
 #pragma unroll
   for (int t = 0; t < G::NQT; ++t) dq[t] = zero16();
 
-  const char* kb = reinterpret_cast<const char*>(a.k) + ((int64_t)k_lo * a.k_stride + (int64_t)kvh * DQK) * 2;
-  const char* vb = reinterpret_cast<const char*>(a.v) + ((int64_t)k_lo * a.v_stride + (int64_t)kvh * DV) * 2;
-  const int64_t ksb = a.k_stride * 2, vsb = a.v_stride * 2;
   const int arow = sigma(l32);
   const int trr = tr_row(lane), trc = tr_col_bytes(lane);
   DualLoader<Q_BN, DQK, G::KROWB, NT / 64> lk;
   DualLoader<Q_BN, DV, G::VROWB, NT / 64> lv;
   lk.init(ksb, wave, lane);
   lv.init(vsb, wave, lane);
-  auto issue = [&](int t, char* kd, char* vd) __attribute__((always_inline)) {
-    const int rows_left = klen - t * Q_BN;
-    lk.issue(kb + (int64_t)t * Q_BN * ksb, ksb, rows_left, kd);
-    lv.issue(vb + (int64_t)t * Q_BN * vsb, vsb, rows_left, vd);
+  auto issue = [&](const Cursor& c, char* kd, char* vd) __attribute__((always_inline)) {
+    const int rows_left = c.blk.klen - c.t * Q_BN;
+    lk.issue(c.blk.kb + (int64_t)c.t * Q_BN * ksb, ksb, rows_left, kd);
+    lv.issue(c.blk.vb + (int64_t)c.t * Q_BN * vsb, vsb, rows_left, vd);
   };
 
-  auto tile = [&](int t, const char* ks, const char* vs) __attribute__((always_inline)) {
-    const int kt0 = t * Q_BN;
-    if (!(wave_live && kt0 < wave_kend)) return;
-    const bool need_mask = (kt0 + Q_BN > wave_kend) || (CAUSAL && kt0 + Q_BN - 1 > wq_first_rel);
+  auto tile = [&](const Cursor& c, const char* ks, const char* vs) __attribute__((always_inline)) {
+    const int kt0 = c.t * Q_BN, klen = c.blk.klen, kind = c.blk.kind;
+    bool live = wave_live, need_mask;
+    int wave_kend = klen;
+    if (kind == QK_CAUSAL) {
+      wave_kend = min(klen, wq_last_rel + 1);
+      live = live && kt0 < wave_kend;
+      need_mask = (kt0 + Q_BN > wave_kend) || (kt0 + Q_BN - 1 > wq_first_rel);
+    } else if (kind == QK_LATE_ROWS) {
+      live = live && wq_last_rel >= qhalf && kt0 < klen;
+      need_mask = (kt0 + Q_BN > klen) || (wq_first_rel < qhalf);
+    } else {
+      live = live && kt0 < klen;
+      need_mask = kt0 + Q_BN > klen;
+    }
+    if (!live) return;
     bf16x8 dsp[4];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -518,7 +635,8 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a) {
         float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -l2));
         if (need_mask) {
           const int key = kt0 + 32 * hh + 16 * (i >> 3) + 8 * g + (i & 7);
-          const bool ok = key < klen && (!CAUSAL || key <= my_row_rel);
+          const bool ok = key < klen && (kind != QK_CAUSAL || key <= my_row_rel) &&
+                          (kind != QK_LATE_ROWS || my_row_rel >= qhalf);
           p = ok ? p : 0.f;
         }
         dp[i] = p * (dp[i] - dl);
@@ -542,15 +660,19 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a) {
     pipeline_lds_mfma<4 * G::NQT, 2, kBwdAhead>();
   };
 
-  // this workgroup's key tiles: j-th is tile kshare + j * nks
-  const int n_mine = ntiles > kshare ? (ntiles - kshare + nks - 1) / nks : 0;
-  if (n_mine > 0) issue(kshare, ks0, vs0);
+  // this workgroup's tiles of the walk: the j-th is walk tile kshare + j * nks
+  const int n_mine = total > kshare ? (total - kshare + nks - 1) / nks : 0;
+  if (n_mine > 0) issue(lc, ks0, vs0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   auto step = [&](int j, const char* ks, const char* vs, char* kn, char* vn)
       __attribute__((always_inline)) {
-    if (j + 1 < n_mine) issue(kshare + (j + 1) * nks, kn, vn);
-    tile(kshare + j * nks, ks, vs);
+    if (j + 1 < n_mine) {
+      advance(lc, nks);
+      issue(lc, kn, vn);
+    }
+    tile(cc, ks, vs);
+    advance(cc, nks);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
@@ -638,14 +760,18 @@ hipError_t launch_attn_bwd_bf16(const AttnArgs& a0, int dqk, int dv, bool causal
   const long long nk = (long long)a.n_seq * a.hkv * ak.n_ktiles * ak.qsplit;
   if (nq > 0x7fffffffLL || nk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (kv_split && dqk != 128) return hipErrorInvalidValue;
+  RankKV no_kv;
+  RankGrad no_grad;
+  memset(&no_kv, 0, sizeof(no_kv));
+  memset(&no_grad, 0, sizeof(no_grad));
 #define RA_BWD_LAUNCH(DQ, DVV, C, QSPLIT)                                                      \
   do {                                                                                         \
     if (nq > 0)                                                                                \
       hipLaunchKernelGGL((attn_bwd_dq_kernel<DQ, DVV, C>), dim3((unsigned)nq), dim3(NT), 0, st, \
-                         a);                                                                   \
+                         a, no_kv);                                                            \
     if (nk > 0)                                                                                \
       hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQ, DVV, C, QSPLIT>), dim3((unsigned)nk),       \
-                         dim3(NT), 0, st, ak);                                                 \
+                         dim3(NT), 0, st, ak, no_kv, no_grad);                                 \
   } while (0)
   if (dqk == 128 && dv == 128) {
     if (kv_split) {
@@ -676,6 +802,45 @@ hipError_t launch_attn_bwd_bf16(const AttnArgs& a0, int dqk, int dv, bool causal
     if (nb > 0)
       hipLaunchKernelGGL(bwd_qsplit_reduce_kernel, dim3((unsigned)nb), dim3(256), 0, st, ak, dqk,
                          dv, total_k);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rank_bwd_bf16(const AttnArgs& a0, const RankKV& rk, const RankGrad& rg, int dqk,
+                                int dv, hipStream_t st) {
+  // a0.n_qtiles counts 128-row query tiles of the local rows, a0.n_ktiles
+  // 128-key tiles of a whole local segment (the largest part of any owner)
+  AttnArgs a = a0;
+  a.q_part = RA_PART_ALL;
+  a.k_part = RA_PART_ALL;
+  a.qsplit = 1;
+  if (a.ksplit < 1 || !a.dq_part) a.ksplit = 1;
+  const long long nq = (long long)a.n_seq * a.hkv * a.n_qtiles * a.group * a.ksplit;
+  const long long nk = (long long)rk.cp * a.n_seq * a.hkv * a.n_ktiles;
+  if (nq > 0x7fffffffLL || nk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (dqk == 128 && dv == 128) {
+    if (nk > 0)
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<128, 128, false, false, true>), dim3((unsigned)nk),
+                         dim3(NT), 0, st, a, rk, rg);
+    if (nq > 0)
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 128, false, true>), dim3((unsigned)nq),
+                         dim3(NT), 0, st, a, rk);
+  } else if (dqk == 192 && dv == 128) {
+    if (nk > 0)
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<192, 128, false, false, true>), dim3((unsigned)nk),
+                         dim3(NT), 0, st, a, rk, rg);
+    if (nq > 0)
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<192, 128, false, true>), dim3((unsigned)nq),
+                         dim3(NT), 0, st, a, rk);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  if (a.ksplit > 1 && nq > 0) {
+    const long long n4 = (long long)a.total_q * a.hq * dqk / 4;
+    const long long nb = (n4 + 255) / 256;
+    if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (nb > 0)
+      hipLaunchKernelGGL(bwd_ksplit_reduce_kernel, dim3((unsigned)nb), dim3(256), 0, st, a, dqk);
   }
   return hipGetLastError();
 }

@@ -81,6 +81,37 @@ struct RankKV {
   int64_t part_out_stride, part_lse_stride;
 };
 
+// dK / dV accumulators of every owner for a rank's fused backward (one
+// dK/dV launch over all owners' key tiles).
+struct RankGrad {
+  float* dk[kMaxCp];
+  float* dv[kMaxCp];
+};
+
+// The block of `owner` in `rank`'s share of a ring of the zig-zag placement:
+// its own block is causal over all rows and keys; an earlier owner's block
+// is seen whole by every row through its first key half only; a later
+// owner's block is seen by the second row half only, over all its keys.
+// (Derived from the global causal rule: the owner's first chunk precedes
+// both of the rank's chunks, its second chunk follows both, and both chunks
+// of a later owner lie between the rank's two.)
+__host__ __device__ inline void owner_plan(int rank, int owner, int* causal, int* q_part,
+                                           int* k_part) {
+  if (owner == rank) {
+    *causal = 1;
+    *q_part = RA_PART_ALL;
+    *k_part = RA_PART_ALL;
+  } else if (owner < rank) {
+    *causal = 0;
+    *q_part = RA_PART_ALL;
+    *k_part = RA_PART_FIRST_HALF;
+  } else {
+    *causal = 0;
+    *q_part = RA_PART_SECOND_HALF;
+    *k_part = RA_PART_ALL;
+  }
+}
+
 // Segment part [lo, hi) after applying a zig-zag half selector.
 __host__ __device__ inline void part_range(int32_t s0, int32_t s1, int32_t part, int32_t* lo,
                                            int32_t* hi) {
@@ -132,6 +163,14 @@ hipError_t launch_bwd_delta(const void* out, int out_dtype, const void* dout, in
                             hipStream_t st);
 hipError_t launch_attn_bwd_bf16(const AttnArgs& a, int dqk, int dv, bool causal, bool kv_split,
                                 int total_k, hipStream_t st);
+// A rank's whole backward share in two launches: dK/dV over every owner's
+// key tiles (each with the owner's plan, into rg's accumulators), and dQ
+// with every query tile walking all owners' key tiles in ring order (dealt
+// over a.ksplit workgroups, partials reduced in share order).  a describes
+// the rank's local rows (q, dout, lse, delta, dq; parts ALL); rk the
+// owners' K/V blocks.
+hipError_t launch_rank_bwd_bf16(const AttnArgs& a, const RankKV& rk, const RankGrad& rg, int dqk,
+                                int dv, hipStream_t st);
 
 // Sets the thread-local message ra_last_error() returns and passes st back.
 ra_status set_error(ra_status st, const char* fmt, ...);

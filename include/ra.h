@@ -291,6 +291,22 @@ ra_status ra_block_attn_bwd(const ra_attn_desc* d, const void* dout, const float
  * float32 partials follow the dK/dV ones in the workspace.  A workspace
  * smaller than that size is rejected with RA_ERR_INVALID_ARG before any
  * launch.
+ *
+ * That is the per-step form.  For packed documents (n_seq > 1) and for
+ * shares of at most 64K (row, head) pairs the share runs rank-fused
+ * instead: one dK/dV launch over the key tiles of every owner's block
+ * (each with that step's rule, added into that owner's dK/dV) and one dQ
+ * launch whose query tiles walk the key tiles of all blocks in ring order,
+ * dQ kept in registers; on shares with few query tiles up to 4 workgroups
+ * deal a query tile's walk, their float32 partials (after delta in the
+ * workspace) added in share order.  The results are the same up to
+ * rounding order; both forms are deterministic.  RA_BWD_RANK_FUSED=0 / =1
+ * in the environment forces one form; ra_rank_backward_workspace reports
+ * the size of the form that will run.
+ * events (optional): host array of 2*cp_size hipEvent_t; events[0] is
+ * recorded before the rank's first launch and events[2*cp_size-1] after its
+ * last in both forms; the per-step form also records events[2s] / [2s+1]
+ * around step s's launches (step 0's span includes the delta launch).
  */
 typedef struct ra_rank_bwd_desc {
   ra_attn_desc local;

@@ -265,6 +265,7 @@ def test_rank_backward_workspace_sizes(qsplit_env, n_parts, monkeypatch):
     most, the same for every rank: for a 32K GQA rank share (4096 local
     tokens, 32/8 heads, d 128) the causal diagonal block and the earlier
     owners' blocks (2048 keys, 128 workgroups of 128 keys) split in two."""
+    monkeypatch.setenv("RA_BWD_RANK_FUSED", "0")      # one pair of launches per step
     if qsplit_env is None:
         monkeypatch.delenv("RA_BWD_QSPLIT", raising=False)
     else:
@@ -282,6 +283,61 @@ def test_rank_backward_workspace_sizes(qsplit_env, n_parts, monkeypatch):
         assert L.lib().ra_rank_backward_workspace(ctypes.byref(rd), ctypes.byref(n)) == 0
         sizes.add(n.value)
     assert sizes == {hq * T * 4 + n_parts * T * hkv * (128 + 128) * 4}
+
+
+@pytest.mark.parametrize("T,hq,hkv,C,ksplit_env,n_parts", [
+    (4096, 32, 8, 8, None, 0),    # 32K GQA rank: 1024 dQ workgroups, no split
+    (2048, 8, 8, 4, None, 1),     # 8K MHA rank: 128 dQ workgroups, split in 2
+    (2048, 8, 8, 4, "4", 3),
+])
+def test_rank_fused_backward_workspace_sizes(T, hq, hkv, C, ksplit_env, n_parts, monkeypatch):
+    """Rank-fused backward: delta [hq, T] plus the float32 dQ partials
+    [T, hq, dqk] of key shares 1 .. ksplit-1, the same for every rank; the
+    dK/dV launch over all owners needs no partials."""
+    monkeypatch.setenv("RA_BWD_RANK_FUSED", "1")
+    if ksplit_env is None:
+        monkeypatch.delenv("RA_BWD_KSPLIT", raising=False)
+    else:
+        monkeypatch.setenv("RA_BWD_KSPLIT", ksplit_env)
+    local = _desc(cu=np.array([0, T], np.int32), hq=hq, hkv=hkv)
+    kb = (ctypes.c_void_p * C)(*([FAKE] * C))
+    sizes = set()
+    for r in range(C):
+        rd = L.RankBwdDesc()
+        rd.local = local
+        rd.cp_size, rd.rank = C, r
+        rd.k_blocks = rd.v_blocks = ctypes.cast(kb, ctypes.c_void_p)
+        n = ctypes.c_size_t(0)
+        assert L.lib().ra_rank_backward_workspace(ctypes.byref(rd), ctypes.byref(n)) == 0
+        sizes.add(n.value)
+    assert sizes == {hq * T * 4 + n_parts * T * hq * 128 * 4}
+
+
+@pytest.mark.parametrize("name,fused", [("mha_8k", True), ("varlen_128k", True),
+                                        ("gqa_32k", False), ("mla_256k", False)])
+def test_rank_backward_form_choice(name, fused, monkeypatch):
+    """Without RA_BWD_RANK_FUSED the rank backward is fused for packed
+    documents and for shares of at most 64K (row, head) pairs, and runs one
+    pair of launches per step otherwise; the workspace follows the form
+    (delta and the fused dQ partials, or delta and the per-step partials)."""
+    w = synth.WORKLOADS[name]
+    cu_local, _ = L.ra_zigzag_shard_map(w.cp, 0, w.cu_global())
+    local = _desc(hq=w.hq, hkv=w.hkv, dqk=w.dqk, dv=w.dv, cu=cu_local)
+    kb = (ctypes.c_void_p * w.cp)(*([FAKE] * w.cp))
+    rd = L.RankBwdDesc()
+    rd.local = local
+    rd.cp_size, rd.rank = w.cp, 0
+    rd.k_blocks = rd.v_blocks = ctypes.cast(kb, ctypes.c_void_p)
+    sizes = {}
+    for env in (None, "1", "0"):
+        if env is None:
+            monkeypatch.delenv("RA_BWD_RANK_FUSED", raising=False)
+        else:
+            monkeypatch.setenv("RA_BWD_RANK_FUSED", env)
+        n = ctypes.c_size_t(0)
+        assert L.lib().ra_rank_backward_workspace(ctypes.byref(rd), ctypes.byref(n)) == 0
+        sizes[env] = n.value
+    assert sizes[None] == sizes["1" if fused else "0"]
 
 
 def test_rank_backward_rejects_short_workspace(monkeypatch):

@@ -201,32 +201,42 @@ def test_mla_backward_reduced_full_parity():
     _full_bwd_parity(synth.reduced("mla_256k", 4096, 8))
 
 
-# Work splits of the rank backward: (RA_BWD_QSPLIT, RA_BWD_KV_SPLIT,
-# RA_BWD_KSPLIT).  qsplit = workgroups sharing a dK/dV key tile, ksplit =
-# workgroups sharing a dQ query tile (partials in the workspace, added in
-# share order); the query split over a workgroup's waves (KV_SPLIT=1) only
-# runs where qsplit is 1.
+# Forms of the rank backward: (RA_BWD_RANK_FUSED, RA_BWD_QSPLIT,
+# RA_BWD_KV_SPLIT, RA_BWD_KSPLIT); "auto" leaves the choice to the library
+# (fused for packed documents and small shares).  Rank-fused ("1"): one dK/dV
+# launch over every owner's key tiles and one dQ launch walking all blocks,
+# ksplit = workgroups sharing a dQ query tile.  Per step ("0"): one pair of
+# launches per ring step; qsplit = workgroups sharing a dK/dV key tile,
+# ksplit = workgroups sharing a dQ query tile (partials in the workspace,
+# added in share order); the query split over a workgroup's waves
+# (KV_SPLIT=1) only runs where qsplit is 1.
 BWD_SPLITS = {
-    "auto": (None, None, None),
-    "qsplit1": ("1", None, "1"),
-    "qsplit1_waves0": ("1", "0", None),
-    "qsplit1_waves1": ("1", "1", None),
-    "qsplit3": ("3", None, None),
-    "qsplit4": ("4", None, None),
-    "ksplit2": (None, None, "2"),
-    "ksplit3_qsplit3": ("3", None, "3"),
-    "ksplit4_qsplit2": ("2", None, "4"),
+    "auto": (None, None, None, None),
+    "fused_ksplit1": ("1", None, None, "1"),
+    "fused_ksplit2": ("1", None, None, "2"),
+    "fused_ksplit3": ("1", None, None, "3"),
+    "fused_ksplit4": ("1", None, None, "4"),
+    "fused_auto": ("1", None, None, None),
+    "step_auto": ("0", None, None, None),
+    "qsplit1": ("0", "1", None, "1"),
+    "qsplit1_waves0": ("0", "1", "0", None),
+    "qsplit1_waves1": ("0", "1", "1", None),
+    "qsplit3": ("0", "3", None, None),
+    "qsplit4": ("0", "4", None, None),
+    "ksplit2": ("0", None, None, "2"),
+    "ksplit3_qsplit3": ("0", "3", None, "3"),
+    "ksplit4_qsplit2": ("0", "2", None, "4"),
 }
 
 
 def _set_splits(monkeypatch, mode):
-    qs, kv, ks = BWD_SPLITS[mode]
-    if qs is not None:
-        monkeypatch.setenv("RA_BWD_QSPLIT", qs)
-    if kv is not None:
-        monkeypatch.setenv("RA_BWD_KV_SPLIT", kv)
-    if ks is not None:
-        monkeypatch.setenv("RA_BWD_KSPLIT", ks)
+    fused, qs, kv, ks = BWD_SPLITS[mode]
+    for name, val in (("RA_BWD_RANK_FUSED", fused), ("RA_BWD_QSPLIT", qs),
+                      ("RA_BWD_KV_SPLIT", kv), ("RA_BWD_KSPLIT", ks)):
+        if val is None:
+            monkeypatch.delenv(name, raising=False)
+        else:
+            monkeypatch.setenv(name, val)
 
 
 @pytest.mark.parametrize("mode", list(BWD_SPLITS))
@@ -235,32 +245,37 @@ def test_gqa_backward_reduced_full_parity(mode, monkeypatch):
     _full_bwd_parity(synth.reduced("gqa_32k", 4096, 8))
 
 
-@pytest.mark.parametrize("mode", ["qsplit1", "qsplit3", "ksplit4_qsplit2"])
+@pytest.mark.parametrize("mode", ["fused_ksplit3", "fused_auto", "qsplit1", "qsplit3",
+                                  "ksplit4_qsplit2"])
 def test_mla_backward_reduced_split_parity(mode, monkeypatch):
     _set_splits(monkeypatch, mode)
     _full_bwd_parity(synth.reduced("mla_256k", 2048, 4))
 
 
-def test_varlen_backward_reduced_split3_parity(monkeypatch):
-    _set_splits(monkeypatch, "ksplit3_qsplit3")
+@pytest.mark.parametrize("mode", ["fused_ksplit3", "ksplit3_qsplit3"])
+def test_varlen_backward_reduced_split3_parity(mode, monkeypatch):
+    _set_splits(monkeypatch, mode)
     w = synth.reduced("varlen_128k", 8192, 4)
     w.doc_lengths = synth.doc_lengths_loguniform(4, 8192, 8, 2048, 8)
     _full_bwd_parity(w)
 
 
-@pytest.mark.parametrize("mode", ["auto", "qsplit1", "ksplit3_qsplit3"])
+@pytest.mark.parametrize("mode", ["auto", "fused_ksplit4", "step_auto", "qsplit1",
+                                  "ksplit3_qsplit3"])
 def test_mha_backward_reduced_full_parity(mode, monkeypatch):
     _set_splits(monkeypatch, mode)
     _full_bwd_parity(synth.reduced("mha_8k", 2048, 4))
 
 
-def test_varlen_backward_reduced_full_parity():
+@pytest.mark.parametrize("mode", ["auto", "step_auto"])
+def test_varlen_backward_reduced_full_parity(mode, monkeypatch):
+    _set_splits(monkeypatch, mode)
     w = synth.reduced("varlen_128k", 8192, 4)
     w.doc_lengths = synth.doc_lengths_loguniform(4, 8192, 8, 2048, 8)
     _full_bwd_parity(w)
 
 
-@pytest.mark.parametrize("mode", ["auto", "qsplit4", "ksplit3_qsplit3"])
+@pytest.mark.parametrize("mode", ["auto", "fused_ksplit3", "qsplit4", "ksplit3_qsplit3"])
 def test_backward_is_deterministic(mode, monkeypatch):
     _set_splits(monkeypatch, mode)
     w = synth.reduced("mla_256k", 2048, 4)

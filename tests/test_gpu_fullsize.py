@@ -5,8 +5,8 @@
   the epilogue), every row and head against the oracle's attention of the
   same global rows.
 * 8K MHA (S=8192, CP=4, 8 heads, d 128) backward at full size with the
-  automatic work splits: every dQ, dK, dV element against the oracle's
-  gradients.
+  automatic work splits, rank-fused and per step: every dQ, dK, dV element
+  against the oracle's gradients.
 * 32K GQA backward at full size: sampled dQ rows of three ranks, dK/dV of
   the last 256 keys in full, and the sum rules over every key.
 * The 16K copy of the 256K MLA workload (S=16384, CP=32: 256-token chunks,
@@ -91,7 +91,7 @@ def test_gqa_32k_backward_sampled_and_sum_rules(gqa_32k, monkeypatch):
     """Full-size backward with the automatic splits: sampled dQ rows of
     ranks 0, 3 and 7, dK/dV of the last 256 keys (seen only by the last 256
     rows, which rank 0 holds), and the sum rules over every key."""
-    for v in ("RA_BWD_QSPLIT", "RA_BWD_KSPLIT", "RA_BWD_KV_SPLIT"):
+    for v in ("RA_BWD_RANK_FUSED", "RA_BWD_QSPLIT", "RA_BWD_KSPLIT", "RA_BWD_KV_SPLIT"):
         monkeypatch.delenv(v, raising=False)
     w, prob, (q64, k64, v64, do64) = gqa_32k
     log(f"gqa_32k backward (full size): S={w.seqlen} C={w.cp}")
@@ -143,9 +143,11 @@ def _concat_grads(prob, dqs, dks, dvs):
     return gq, gk, gv
 
 
-def _full_backward(w, monkeypatch):
-    for v in ("RA_BWD_QSPLIT", "RA_BWD_KSPLIT", "RA_BWD_KV_SPLIT"):
+def _full_backward(w, monkeypatch, fused=True):
+    for v in ("RA_BWD_RANK_FUSED", "RA_BWD_QSPLIT", "RA_BWD_KSPLIT", "RA_BWD_KV_SPLIT"):
         monkeypatch.delenv(v, raising=False)
+    if not fused:
+        monkeypatch.setenv("RA_BWD_RANK_FUSED", "0")
     log(f"{w.name} backward in full: S={w.seqlen} C={w.cp} hq={w.hq} d={w.dqk}/{w.dv}")
     prob, (q, k, v, do) = make_problem(w, with_dout=True)
     q64, k64, v64, do64 = to_np(q), to_np(k), to_np(v), to_np(do)
@@ -157,8 +159,10 @@ def _full_backward(w, monkeypatch):
     check_out(gv, rv, "bf16", "dV (every element)")
 
 
-def test_mha_8k_backward_full_parity(monkeypatch):
-    _full_backward(synth.WORKLOADS["mha_8k"], monkeypatch)
+@pytest.mark.parametrize("fused", [True, False], ids=["rank_fused", "per_step"])
+def test_mha_8k_backward_full_parity(fused, monkeypatch):
+    """Both forms of the rank backward, with their automatic splits."""
+    _full_backward(synth.WORKLOADS["mha_8k"], monkeypatch, fused)
 
 
 def _mla_mini():
