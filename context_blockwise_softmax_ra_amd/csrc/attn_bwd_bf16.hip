@@ -188,8 +188,27 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a, RankKV
   const int arow = sigma(l32);  // A-operand row of this lane (query row in the tile)
   const int trr = tr_row(lane), trc = tr_col_bytes(lane);
 
-  auto it_head = [&](int it) { return kvh * a.group + it / per_head; };
-  auto it_q0 = [&](int it) { return q_lo + (qt_begin + it % per_head) * KV_BQ; };
+  // Iteration it is query head it / per_head of the group and query tile
+  // qt_begin + it % per_head; the loop steps a (head, tile) cursor instead
+  // of dividing by the runtime per_head twice per iteration (a software
+  // division is some 40 scalar instructions, on the only wave of the SIMD).
+  struct ItPos {
+    int h, qt;  // head within the group, tile index from qt_begin
+  };
+  auto it_pos = [&](int it) {
+    ItPos c;
+    c.h = per_head > 0 ? it / per_head : 0;
+    c.qt = per_head > 0 ? it - c.h * per_head : 0;
+    return c;
+  };
+  auto it_next = [&](ItPos c, int n) {
+    c.qt += n;
+    while (c.qt >= per_head) {
+      c.qt -= per_head;
+      ++c.h;
+    }
+    return c;
+  };
   // with QS each wave loads its own tiles alone
   DualLoader<KV_BQ, DQK, G::QROWB, QS ? 1 : NT / 64> lq;
   DualLoader<KV_BQ, DV, G::OROWB, QS ? 1 : NT / 64> lo;
@@ -198,8 +217,9 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a, RankKV
   lo.init(osb, QS ? 0 : wave, lane);
   // tile it's Q, dO, lse and delta into one stage (rows past the part are
   // clamped to its last row here and masked in the products)
-  auto issue = [&](int it, char* qd, char* od, float* ldd) __attribute__((always_inline)) {
-    const int h = it_head(it), q0 = it_q0(it), rows_left = q_hi - q0;
+  auto issue = [&](ItPos c, char* qd, char* od, float* ldd) __attribute__((always_inline)) {
+    const int h = kvh * a.group + c.h, q0 = q_lo + (qt_begin + c.qt) * KV_BQ;
+    const int rows_left = q_hi - q0;
     lq.issue(reinterpret_cast<const char*>(a.q) + ((int64_t)q0 * a.q_stride + (int64_t)h * DQK) * 2,
              qsb, rows_left, qd);
     lo.issue(reinterpret_cast<const char*>(a.dout) + ((int64_t)q0 * a.hq + h) * DV * 2, osb,
@@ -213,9 +233,9 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a, RankKV
   };
 
   // products of tile it from one stage
-  auto tile = [&](int it, const char* qs, const char* os, const float* lsd)
+  auto tile = [&](ItPos c, const char* qs, const char* os, const float* lsd)
       __attribute__((always_inline)) {
-    const int qt_rel = (qt_begin + it % per_head) * KV_BQ;  // first query row (part-relative)
+    const int qt_rel = (qt_begin + c.qt) * KV_BQ;  // first query row (part-relative)
     const bool live = wave_live && (!causal || qt_rel + KV_BQ - 1 >= wk_rel);
     if (!live) return;
     // S = Q K^T and dP = dO V^T, lane = key column, entry i = query row
@@ -277,13 +297,16 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a, RankKV
   // iterations of this wave: all (it += 1), or with QS every 4th from the
   // wave's index
   const int it0 = it_lo + (QS ? wave : 0), istep = QS ? NT / 64 : 1;
-  if (it0 < n_it) issue(it0, qs0[ws], os0[ws], ld0[ws]);
+  ItPos pos = it_pos(it0);  // of iteration it
+  if (it0 < n_it) issue(pos, qs0[ws], os0[ws], ld0[ws]);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();  // V (and, without QS, the first tile) in LDS
   auto step = [&](int it, const char* qs, const char* os, const float* lsd, char* qn, char* on,
                   float* ln) __attribute__((always_inline)) {
-    if (it + istep < n_it) issue(it + istep, qn, on, ln);
-    tile(it, qs, os, lsd);
+    const ItPos next = it_next(pos, istep);
+    if (it + istep < n_it) issue(next, qn, on, ln);
+    tile(pos, qs, os, lsd);
+    pos = next;
     // next tile landed (own loads); without QS also every wave is done with
     // this one (with QS the stages are the wave's own, and its reads of
     // them complete before it issues the next load into them)
