@@ -57,9 +57,12 @@ def test_rank_forward_graph_replays(fuse):
         log(f"  replay {i}: every rank bit-identical to eager")
 
 
-def test_rank_backward_graph_replays():
+@pytest.mark.parametrize("form", ["1", "0"], ids=["rank_fused", "per_step"])
+def test_rank_backward_graph_replays(form, monkeypatch):
+    monkeypatch.setenv("RA_BWD_RANK_FUSED", form)
     w = synth.reduced("mla_256k", 2048, 4)
-    log(f"backward graph: S={w.seqlen} C={w.cp} d={w.dqk}/{w.dv}")
+    log(f"backward graph ({'rank-fused' if form == '1' else 'per step'}): S={w.seqlen} "
+        f"C={w.cp} d={w.dqk}/{w.dv}")
     prob, _ = make_problem(w, with_dout=True)
     outs, lses = [], []
     for r in range(prob.cp):

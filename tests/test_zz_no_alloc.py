@@ -82,3 +82,38 @@ def test_noalloc_rejects_shares_beyond_the_scratch():
         L.ra_rank_forward_noalloc(rd)
     assert e.value.status == L.RA_ERR_INVALID_ARG
     assert "fixed scratch" in str(e.value)
+
+
+def test_noalloc_under_graph_capture(monkeypatch):
+    """Captured in a HIP graph (one of the callers the entry point is for),
+    the allocation-free rank forward replays bit-identical to the eager
+    call, with eager work on the same output buffers between replays."""
+    monkeypatch.delenv("RA_FWD_KV_SPLIT", raising=False)
+    monkeypatch.delenv("RA_FWD_KERNEL", raising=False)
+    w = synth.WORKLOADS["mha_8k"]
+    prob, _ = make_problem(w)
+    outs = [prob.alloc_forward(torch.bfloat16, 2)[:2] for _ in range(prob.cp)]
+    for r in range(prob.cp):
+        L.ra_rank_forward_noalloc(prob.forward_desc(r, *outs[r], None, 2))
+    torch.cuda.synchronize()
+    ref = [(o.clone(), l.clone()) for o, l in outs]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=side):
+        # torch.cuda.graph makes `side` current while it captures
+        for r in range(prob.cp):
+            L.ra_rank_forward_noalloc(prob.forward_desc(r, *outs[r], None, 2), side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for i in range(3):
+        for o, l in outs:
+            o.fill_(float("nan"))
+            l.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for r in range(prob.cp):
+            assert torch.equal(outs[r][0], ref[r][0]) and torch.equal(outs[r][1], ref[r][1]), \
+                (i, r)
+        log(f"  replay {i}: every rank bit-identical to eager")
