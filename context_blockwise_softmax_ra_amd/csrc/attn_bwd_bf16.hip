@@ -238,6 +238,16 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a, RankKV
     const int qt_rel = (qt_begin + c.qt) * KV_BQ;  // first query row (part-relative)
     const bool live = wave_live && (!causal || qt_rel + KV_BQ - 1 >= wk_rel);
     if (!live) return;
+    // lse and delta of the lane's 16 rows (entry i below is row 16(i/8) +
+    // 8g + i%8), read before the products so their latency hides there
+    float4 lr[4], dr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * (j >> 1) + 8 * g + 4 * (j & 1);
+      lr[j] = *reinterpret_cast<const float4*>(lsd + r);
+      dr[j] = *reinterpret_cast<const float4*>(lsd + KV_BQ + r);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     // S = Q K^T and dP = dO V^T, lane = key column, entry i = query row
     // 16*(i/8) + 8g + i%8 of the tile
     f32x16 s = zero16(), dp = zero16();
@@ -250,24 +260,37 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a, RankKV
                as_bf16x8(lds16(vsm + dual_off<G::OROWB>(vrow, (16 * kk + 8 * g) * 2))), dp);
     pipeline_lds_mfma_n<G::KK, 1, G::VK, 2, kBwdAhead>();
     __builtin_amdgcn_sched_barrier(0);
-    const bool need_mask = (my_key_rel >= klen) || (wk_rel + 31 >= klen) ||
-                           (causal && qt_rel < wk_rel + 31) || (qt_rel + KV_BQ > qlen);
-    // A row that sees nothing (lse = -inf) only occurs in a masked tile:
-    // every pair of an unmasked tile is visible.  Its exp overflows to inf
-    // and the mask then replaces P by 0, so lse needs no guard.
+    // wave-uniform: some pair of the tile is hidden (the wave's last key past
+    // the part covers every lane's key past it)
+    const bool need_mask = (wk_rel + 31 >= klen) || (causal && qt_rel < wk_rel + 31) ||
+                           (qt_rel + KV_BQ > qlen);
+    float nl2[16], dl[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int r = 16 * (i >> 3) + 8 * g + (i & 7);
-      const float l2 = lsd[r] * kLog2e;
-      const float dl = lsd[KV_BQ + r];
-      float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -l2));
-      if (need_mask) {
-        const bool ok = (my_key_rel < klen) && (qt_rel + r < qlen) &&
-                        (!causal || my_key_rel <= qt_rel + r);
-        p = ok ? p : 0.f;
+      nl2[i] = -lr[i >> 2][i & 3] * kLog2e;
+      dl[i] = dr[i >> 2][i & 3];
+    }
+    if (need_mask) {
+      // Hidden pairs get score -inf, so P = 0.  A row that sees nothing
+      // (lse -inf, which only a masked tile holds: every pair of an
+      // unmasked tile is visible) gets offset -inf instead of +inf.  Entry i
+      // is row 8g + e of the tile, e = 16(i/8) + i%8; it is visible iff
+      // lo <= e < hi.
+      const int r0 = qt_rel + 8 * g;
+      const int hi = my_key_rel < klen ? qlen - r0 : -1;
+      const int lo = causal ? my_key_rel - r0 : -KV_BQ;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int e = 16 * (i >> 3) + (i & 7);
+        s[i] = (e >= lo && e < hi) ? s[i] : -INFINITY;
+        nl2[i] = nl2[i] == INFINITY ? -INFINITY : nl2[i];
       }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, nl2[i]));
       s[i] = p;
-      dp[i] = p * (dp[i] - dl);
+      dp[i] = p * (dp[i] - dl[i]);
     }
     const bf16x8 pp0 = pack8(s, 0), pp1 = pack8(s, 8);
     const bf16x8 ds0 = pack8(dp, 0), ds1 = pack8(dp, 8);
@@ -653,15 +676,23 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a, RankKV r
                  as_bf16x8(lds16(osm + dual_off<G::VROWB>(orow, (16 * kk + 8 * g) * 2))), dp);
       pipeline_lds_mfma_n<G::KK, 1, G::VK, 2, kBwdAhead>();
       __builtin_amdgcn_sched_barrier(0);
+      if (need_mask) {
+        // hidden pairs get score -inf (P = 0; a row outside the part already
+        // has offset -inf).  Entry i is key base + e of the block, e =
+        // 16(i/8) + i%8; every rule of the lane's row folds into e <= lim.
+        const int base = kt0 + 32 * hh + 8 * g;
+        int lim = klen - 1 - base;
+        if (kind == QK_CAUSAL) lim = min(lim, my_row_rel - base);
+        if (kind == QK_LATE_ROWS && my_row_rel < qhalf) lim = -1;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int e = 16 * (i >> 3) + (i & 7);
+          s[i] = e <= lim ? s[i] : -INFINITY;
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -l2));
-        if (need_mask) {
-          const int key = kt0 + 32 * hh + 16 * (i >> 3) + 8 * g + (i & 7);
-          const bool ok = key < klen && (kind != QK_CAUSAL || key <= my_row_rel) &&
-                          (kind != QK_LATE_ROWS || my_row_rel >= qhalf);
-          p = ok ? p : 0.f;
-        }
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -l2));
         dp[i] = p * (dp[i] - dl);
       }
       dsp[2 * hh] = pack8(dp, 0);
