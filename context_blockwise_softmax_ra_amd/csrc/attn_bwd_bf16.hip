@@ -11,13 +11,13 @@
 // exactly as in the forward).  Two launches, no atomics, deterministic:
 //
 // dK/dV kernel -- workgroup = 128 keys of one kv head (4 waves x 32 keys).
-//   K of the wave's keys stays in registers, V of the workgroup's keys in
-//   LDS (loaded once); the loop walks every
+//   K and (at d_qk = 128) V of the wave's keys stay in registers, V
+//   otherwise in LDS (loaded once); the loop walks every
 //   query head of the kv group and every 32-row query tile of the segment
 //   part (causal: only tiles at or below the keys).  Per tile, with lane l
 //   owning key column l%32 of the 32x32 accumulators:
-//     S  = Q K^T, dP = dO V^T        A = Q / dO rows from LDS, B = K regs /
-//                                    V rows from LDS
+//     S  = Q K^T, dP = dO V^T        A = Q / dO rows from LDS, B = K / V
+//                                    in registers (V in LDS at d_qk = 192)
 //     dV += P^T dO, dK += dS^T Q     A = P^T / dS^T straight from the S / dP
 //                                    accumulators (query rows fed in the
 //                                    permuted order sigma so 8 consecutive
@@ -26,8 +26,9 @@
 // dQ kernel -- workgroup = 128 query rows of one head (4 waves x 32 rows),
 //   the forward's shape: lane l owns query row l%32; per 64-key tile
 //     S^T = K Q^T, dP^T = V dO^T     A = K / V rows from LDS (sigma order),
-//                                    B = Q held in registers / dO rows of
-//                                    the workgroup in LDS (loaded once)
+//                                    B = Q / dO of the lane's row, held in
+//                                    registers (dO of the workgroup's rows
+//                                    in LDS at d_qk = 192)
 //     dQ^T += K^T dS^T               A = K via transposing LDS reads.
 // Q, dO and K tiles are read both by 128-bit row reads and by transposing
 // reads, so they use the XOR-swizzled "dual" LDS layout (conflict-free for
@@ -104,8 +105,13 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a, RankKV
   __shared__ __attribute__((aligned(1024))) char os1[NS][G::O_BYTES];
   __shared__ __attribute__((aligned(256))) float ld0[NS][2 * KV_BQ];
   __shared__ __attribute__((aligned(256))) float ld1[NS][2 * KV_BQ];
-  // V of the workgroup's keys (dual layout): read as B operands of dP
-  __shared__ __attribute__((aligned(1024))) char vsm[KBN * G::OROWB];
+  // V of the wave's keys as B operands of dP: held in registers at d_qk =
+  // 128 (re-read from LDS every tile it had been a fifth of the tile's LDS
+  // operand bytes); at d_qk = 192 the registers are nearly full (holding it
+  // there cost the MLA backward 9%), so V of the workgroup's keys sits in
+  // LDS (dual layout)
+  constexpr bool VREG = DQK <= 128;
+  __shared__ __attribute__((aligned(1024))) char vsm[VREG ? 16 : KBN * G::OROWB];
 
   const int nsp = QS || RANK ? 1 : a.qsplit;  // workgroups sharing a key tile
   // One block: packed documents deal key tiles (with their query shares)
@@ -156,19 +162,26 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a, RankKV
   const int my_key_rel = wk_rel + l32;               // this lane's key column
   const int my_key = min(k_lo + my_key_rel, k_hi - 1);
 
-  // K of this lane's key as B operands (k = dims 16kk + 8g .. +7); V of the
-  // workgroup's keys goes to LDS (keys past the block re-read the last one)
-  bf16x8 kf[G::KK];
+  // K (and V) of this lane's key as B operands (k = dims 16kk + 8g .. +7;
+  // keys past the block re-read the last one)
+  bf16x8 kf[G::KK], vf[VREG ? G::VK : 1];
   {
     const __bf16* kp = reinterpret_cast<const __bf16*>(kptr) + (int64_t)my_key * a.k_stride +
                        (int64_t)kvh * DQK + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < G::KK; ++kk) kf[kk] = as_bf16x8(ldg16(kp + 16 * kk));
-    DualLoader<KBN, DV, G::OROWB, NT / 64> lvk;
-    const int64_t vsb = a.v_stride * 2;
-    lvk.init(vsb, wave, lane);
-    lvk.issue(reinterpret_cast<const char*>(vptr) + ((int64_t)k0 * a.v_stride + (int64_t)kvh * DV) * 2,
-              vsb, k_hi - k0, vsm);
+    if constexpr (VREG) {
+      const __bf16* vp = reinterpret_cast<const __bf16*>(vptr) + (int64_t)my_key * a.v_stride +
+                         (int64_t)kvh * DV + 8 * g;
+#pragma unroll
+      for (int kk = 0; kk < G::VK; ++kk) vf[kk] = as_bf16x8(ldg16(vp + 16 * kk));
+    } else {
+      DualLoader<KBN, DV, G::OROWB, NT / 64> lvk;
+      const int64_t vsb = a.v_stride * 2;
+      lvk.init(vsb, wave, lane);
+      lvk.issue(reinterpret_cast<const char*>(vptr) + ((int64_t)k0 * a.v_stride + (int64_t)kvh * DV) * 2,
+                vsb, k_hi - k0, vsm);
+    }
   }
   const int vrow = (QS ? 0 : wave * 32) + l32;  // this lane's key row in vsm
   f32x16 dk[G::NQT], dv[G::NVT];
@@ -254,11 +267,18 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a, RankKV
 #pragma unroll
     for (int kk = 0; kk < G::KK; ++kk)
       s = mma(as_bf16x8(lds16(qs + dual_off<G::QROWB>(arow, (16 * kk + 8 * g) * 2))), kf[kk], s);
+    if constexpr (VREG) {
 #pragma unroll
-    for (int kk = 0; kk < G::VK; ++kk)
-      dp = mma(as_bf16x8(lds16(os + dual_off<G::OROWB>(arow, (16 * kk + 8 * g) * 2))),
-               as_bf16x8(lds16(vsm + dual_off<G::OROWB>(vrow, (16 * kk + 8 * g) * 2))), dp);
-    pipeline_lds_mfma_n<G::KK, 1, G::VK, 2, kBwdAhead>();
+      for (int kk = 0; kk < G::VK; ++kk)
+        dp = mma(as_bf16x8(lds16(os + dual_off<G::OROWB>(arow, (16 * kk + 8 * g) * 2))), vf[kk], dp);
+      pipeline_lds_mfma<G::KK + G::VK, 1, kBwdAhead>();
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < G::VK; ++kk)
+        dp = mma(as_bf16x8(lds16(os + dual_off<G::OROWB>(arow, (16 * kk + 8 * g) * 2))),
+                 as_bf16x8(lds16(vsm + dual_off<G::OROWB>(vrow, (16 * kk + 8 * g) * 2))), dp);
+      pipeline_lds_mfma_n<G::KK, 1, G::VK, 2, kBwdAhead>();
+    }
     __builtin_amdgcn_sched_barrier(0);
     // wave-uniform: some pair of the tile is hidden (the wave's last key past
     // the part covers every lane's key past it)
@@ -323,7 +343,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a, RankKV
   ItPos pos = it_pos(it0);  // of iteration it
   if (it0 < n_it) issue(pos, qs0[ws], os0[ws], ld0[ws]);
   __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();  // V (and, without QS, the first tile) in LDS
+  __syncthreads();  // K, V and (without QS) the first tile in place
   auto step = [&](int it, const char* qs, const char* os, const float* lsd, char* qn, char* on,
                   float* ln) __attribute__((always_inline)) {
     const ItPos next = it_next(pos, istep);
@@ -501,8 +521,13 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a, RankKV r
   __shared__ __attribute__((aligned(1024))) char ks1[G::K_BYTES];
   __shared__ __attribute__((aligned(1024))) char vs0[G::V_BYTES];
   __shared__ __attribute__((aligned(1024))) char vs1[G::V_BYTES];
-  // dO of the workgroup's 128 query rows (dual layout): B operands of dP^T
-  __shared__ __attribute__((aligned(1024))) char osm[Q_BM * G::VROWB];
+  // dO of the lane's row as B operands of dP^T: held in registers at d_qk
+  // = 128 (re-read from LDS every tile it had been a quarter of the tile's
+  // LDS operand bytes); at d_qk = 192 the registers are nearly full (holding
+  // it there cost the MLA backward 5%), so dO of the workgroup's 128 rows
+  // sits in LDS (dual layout)
+  constexpr bool OREG = DQK <= 128;
+  __shared__ __attribute__((aligned(1024))) char osm[OREG ? 16 : Q_BM * G::VROWB];
 
   // One block of packed documents: deal query tiles (a kv group's heads and
   // their key shares together) over the XCDs; otherwise contiguous ranges
@@ -610,19 +635,26 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a, RankKV r
   Cursor lc = cc;          // tile to load
 
   const int row = min(my_row, q_hi - 1);
-  // Q of this lane's row as B operands (k = dims 16kk + 8g .. +7); dO of the
-  // workgroup's rows goes to LDS (rows past the part re-read the last one)
-  bf16x8 qf[G::KK];
+  // Q (and dO) of this lane's row as B operands (k = dims 16kk + 8g .. +7;
+  // rows past the part re-read the last one)
+  bf16x8 qf[G::KK], of[OREG ? G::VK : 1];
   {
     const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + (int64_t)row * a.q_stride +
                        (int64_t)h * DQK + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < G::KK; ++kk) qf[kk] = as_bf16x8(ldg16(qp + 16 * kk));
-    DualLoader<Q_BM, DV, G::VROWB, NT / 64> lod;
-    const int64_t osb = (int64_t)a.hq * DV * 2;
-    lod.init(osb, wave, lane);
-    lod.issue(reinterpret_cast<const char*>(a.dout) + ((int64_t)q0 * a.hq + h) * DV * 2, osb,
-              q_hi - q0, osm);
+    if constexpr (OREG) {
+      const __bf16* op =
+          reinterpret_cast<const __bf16*>(a.dout) + ((int64_t)row * a.hq + h) * DV + 8 * g;
+#pragma unroll
+      for (int kk = 0; kk < G::VK; ++kk) of[kk] = as_bf16x8(ldg16(op + 16 * kk));
+    } else {
+      DualLoader<Q_BM, DV, G::VROWB, NT / 64> lod;
+      const int64_t osb = (int64_t)a.hq * DV * 2;
+      lod.init(osb, wave, lane);
+      lod.issue(reinterpret_cast<const char*>(a.dout) + ((int64_t)q0 * a.hq + h) * DV * 2, osb,
+                q_hi - q0, osm);
+    }
   }
   const int orow = wave * 32 + l32;  // this lane's query row in osm
   const int64_t li = (int64_t)h * a.total_q + row;
@@ -670,11 +702,18 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a, RankKV r
 #pragma unroll
       for (int kk = 0; kk < G::KK; ++kk)
         s = mma(as_bf16x8(lds16(ks + dual_off<G::KROWB>(kr, (16 * kk + 8 * g) * 2))), qf[kk], s);
+      if constexpr (OREG) {
 #pragma unroll
-      for (int kk = 0; kk < G::VK; ++kk)
-        dp = mma(as_bf16x8(lds16(vs + dual_off<G::VROWB>(kr, (16 * kk + 8 * g) * 2))),
-                 as_bf16x8(lds16(osm + dual_off<G::VROWB>(orow, (16 * kk + 8 * g) * 2))), dp);
-      pipeline_lds_mfma_n<G::KK, 1, G::VK, 2, kBwdAhead>();
+        for (int kk = 0; kk < G::VK; ++kk)
+          dp = mma(as_bf16x8(lds16(vs + dual_off<G::VROWB>(kr, (16 * kk + 8 * g) * 2))), of[kk], dp);
+        pipeline_lds_mfma<G::KK + G::VK, 1, kBwdAhead>();
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < G::VK; ++kk)
+          dp = mma(as_bf16x8(lds16(vs + dual_off<G::VROWB>(kr, (16 * kk + 8 * g) * 2))),
+                   as_bf16x8(lds16(osm + dual_off<G::VROWB>(orow, (16 * kk + 8 * g) * 2))), dp);
+        pipeline_lds_mfma_n<G::KK, 1, G::VK, 2, kBwdAhead>();
+      }
       __builtin_amdgcn_sched_barrier(0);
       if (need_mask) {
         // hidden pairs get score -inf (P = 0; a row outside the part already
