@@ -57,6 +57,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 #define RA_BWD_AHEAD 4
 #endif
 constexpr int kBwdAhead = RA_BWD_AHEAD;
+// vector instructions of the softmax of one 32-key half in the dQ kernel
+// (per score: two accumulator reads, fma, exp, sub, mul; one pack per two),
+// spread over the products it is interleaved with
+constexpr int kSoftmaxValu = 16 * 6 + 8;
 
 __device__ __forceinline__ float lse_log2(const float* lse, int64_t i, bool valid) {
   // rows outside the part (or that see nothing) contribute P = 0
@@ -694,63 +698,102 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a, RankKV r
       need_mask = kt0 + Q_BN > klen;
     }
     if (!live) return;
+    // Two 32-key halves of the tile: S^T, dP^T products of half hh, its
+    // mask and softmax (dS^T packed into dsp[2hh], dsp[2hh + 1]), then the
+    // dQ products of key blocks bb (16 keys each, half bb / 2).
+    f32x16 s[2], dp[2];
     bf16x8 dsp[4];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      f32x16 s = zero16(), dp = zero16();
+    auto sdp_products = [&](int hh) __attribute__((always_inline)) {
+      s[hh] = zero16();
+      dp[hh] = zero16();
       const int kr = arow + 32 * hh;
 #pragma unroll
       for (int kk = 0; kk < G::KK; ++kk)
-        s = mma(as_bf16x8(lds16(ks + dual_off<G::KROWB>(kr, (16 * kk + 8 * g) * 2))), qf[kk], s);
-      if constexpr (OREG) {
+        s[hh] = mma(as_bf16x8(lds16(ks + dual_off<G::KROWB>(kr, (16 * kk + 8 * g) * 2))), qf[kk], s[hh]);
 #pragma unroll
-        for (int kk = 0; kk < G::VK; ++kk)
-          dp = mma(as_bf16x8(lds16(vs + dual_off<G::VROWB>(kr, (16 * kk + 8 * g) * 2))), of[kk], dp);
-        pipeline_lds_mfma<G::KK + G::VK, 1, kBwdAhead>();
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < G::VK; ++kk)
-          dp = mma(as_bf16x8(lds16(vs + dual_off<G::VROWB>(kr, (16 * kk + 8 * g) * 2))),
-                   as_bf16x8(lds16(osm + dual_off<G::VROWB>(orow, (16 * kk + 8 * g) * 2))), dp);
-        pipeline_lds_mfma_n<G::KK, 1, G::VK, 2, kBwdAhead>();
+      for (int kk = 0; kk < G::VK; ++kk) {
+        const bf16x8 ob = OREG ? of[OREG ? kk : 0]
+                               : as_bf16x8(lds16(osm + dual_off<G::VROWB>(orow, (16 * kk + 8 * g) * 2)));
+        dp[hh] = mma(as_bf16x8(lds16(vs + dual_off<G::VROWB>(kr, (16 * kk + 8 * g) * 2))), ob, dp[hh]);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      if (need_mask) {
-        // hidden pairs get score -inf (P = 0; a row outside the part already
-        // has offset -inf).  Entry i is key base + e of the block, e =
-        // 16(i/8) + i%8; every rule of the lane's row folds into e <= lim.
-        const int base = kt0 + 32 * hh + 8 * g;
-        int lim = klen - 1 - base;
-        if (kind == QK_CAUSAL) lim = min(lim, my_row_rel - base);
-        if (kind == QK_LATE_ROWS && my_row_rel < qhalf) lim = -1;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int e = 16 * (i >> 3) + (i & 7);
-          s[i] = e <= lim ? s[i] : -INFINITY;
-        }
-      }
+    };
+    auto mask_half = [&](int hh) __attribute__((always_inline)) {
+      if (!need_mask) return;
+      // hidden pairs get score -inf (P = 0; a row outside the part already
+      // has offset -inf).  Entry i is key base + e of the block, e =
+      // 16(i/8) + i%8; every rule of the lane's row folds into e <= lim.
+      const int base = kt0 + 32 * hh + 8 * g;
+      int lim = klen - 1 - base;
+      if (kind == QK_CAUSAL) lim = min(lim, my_row_rel - base);
+      if (kind == QK_LATE_ROWS && my_row_rel < qhalf) lim = -1;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -l2));
-        dp[i] = p * (dp[i] - dl);
+        const int e = 16 * (i >> 3) + (i & 7);
+        s[hh][i] = e <= lim ? s[hh][i] : -INFINITY;
       }
-      dsp[2 * hh] = pack8(dp, 0);
-      dsp[2 * hh + 1] = pack8(dp, 8);
+    };
+    auto softmax_half = [&](int hh) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[hh][i], c2, -l2));
+        dp[hh][i] = p * (dp[hh][i] - dl);
+      }
+      dsp[2 * hh] = pack8(dp[hh], 0);
+      dsp[2 * hh + 1] = pack8(dp[hh], 8);
+    };
+    // dQ^T += K^T dS^T over key blocks [bb0, bb1), A = K^T by transposing
+    // reads of the K tile
+    auto dq_products = [&](int bb0, int bb1) __attribute__((always_inline)) {
+#pragma unroll
+      for (int bb = bb0; bb < bb1; ++bb) {
+        const int r = 16 * bb + trr;
+#pragma unroll
+        for (int nt = 0; nt < G::NQT; ++nt) {
+          const int col = 64 * nt + trc;
+          const bf16x8 ka = cat_tr(lds_tr(ks + dual_off<G::KROWB>(r, col)),
+                                   lds_tr(ks + dual_off<G::KROWB>(r + 4, col)));
+          dq[nt] = mma(ka, dsp[bb], dq[nt]);
+        }
+      }
+    };
+    constexpr int NSD = G::KK + G::VK;  // S^T and dP^T products of a half
+    if constexpr (OREG) {
+      // One wave per SIMD: the softmax of a half issues between products it
+      // does not feed (half 0 beside the S^T/dP^T products of half 1, half
+      // 1 beside the dQ products of half 0), so the vector work runs while
+      // the matrix core does.
+      sdp_products(0);
+      pipeline_lds_mfma<NSD, 1, kBwdAhead>();
       __builtin_amdgcn_sched_barrier(0);
-    }
-    // dQ^T += K^T dS^T, A = K^T by transposing reads of the K tile
+      mask_half(0);
+      sdp_products(1);
+      softmax_half(0);
+      pipeline_lds_mfma_valu<NSD, 1, kBwdAhead, kSoftmaxValu / NSD + 1>();
+      keep_here(dsp[0]);
+      keep_here(dsp[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      mask_half(1);
+      dq_products(0, 2);
+      softmax_half(1);
+      pipeline_lds_mfma_valu<2 * G::NQT, 2, kBwdAhead, kSoftmaxValu / (2 * G::NQT) + 1>();
+      keep_here(dsp[2]);
+      keep_here(dsp[3]);
+      __builtin_amdgcn_sched_barrier(0);
+      dq_products(2, 4);
+      pipeline_lds_mfma<2 * G::NQT, 2, kBwdAhead>();
+    } else {
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-      const int r = 16 * bb + trr;
-#pragma unroll
-      for (int nt = 0; nt < G::NQT; ++nt) {
-        const int col = 64 * nt + trc;
-        const bf16x8 ka = cat_tr(lds_tr(ks + dual_off<G::KROWB>(r, col)),
-                                 lds_tr(ks + dual_off<G::KROWB>(r + 4, col)));
-        dq[nt] = mma(ka, dsp[bb], dq[nt]);
+      for (int hh = 0; hh < 2; ++hh) {
+        sdp_products(hh);
+        pipeline_lds_mfma_n<G::KK, 1, G::VK, 2, kBwdAhead>();
+        __builtin_amdgcn_sched_barrier(0);
+        mask_half(hh);
+        softmax_half(hh);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      dq_products(0, 4);
+      pipeline_lds_mfma<4 * G::NQT, 2, kBwdAhead>();
     }
-    pipeline_lds_mfma<4 * G::NQT, 2, kBwdAhead>();
   };
 
   // this workgroup's tiles of the walk: the j-th is walk tile kshare + j * nks

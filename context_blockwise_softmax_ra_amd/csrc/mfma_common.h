@@ -151,6 +151,27 @@ __device__ __forceinline__ void pipeline_lds_mfma_n() {
   __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
 }
 
+// As pipeline_lds_mfma, with up to VPM vector-ALU instructions placed after
+// each product: independent vector work of the same wave (a softmax the
+// products do not feed) then issues while the matrix core runs.
+template <int NM, int RPM, int AHEAD, int VPM>
+__device__ __forceinline__ void pipeline_lds_mfma_valu() {
+  static_assert(AHEAD <= NM, "read-ahead beyond the block");
+  __builtin_amdgcn_sched_group_barrier(0x100, RPM * AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i < NM - AHEAD) __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+  }
+}
+
+// Keeps the computation of v ahead of this point: an empty asm statement
+// that reads it.  Without it the compiler sinks work whose result is used
+// only after a branch into the block past the branch, away from the
+// products it was scheduled beside.
+__device__ __forceinline__ void keep_here(const bf16x8& v) { asm volatile("" : : "v"(v)); }
+
 // Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group,
 // lane i receives element i%4 of the 8 bytes addressed by lane 4r + i/4,
 // r = 0..3.
