@@ -307,6 +307,61 @@ __global__ __launch_bounds__(NT) void split_combine_kernel(
   }
 }
 
+// The same for S parts and rows of DV4 float4 (a power of two): each
+// thread reads its row's S lse values once, and the row index comes from a
+// shift and one 32-bit division (the generic kernel above divides in 64
+// bits twice per float4).
+template <int S, int DV4>
+__global__ __launch_bounds__(NT) void split_combine_fixed_kernel(
+    const float* __restrict__ part_out, const float* __restrict__ part_lse, int64_t po, int64_t pl,
+    void* __restrict__ out, int out_bf16, float* __restrict__ lse, uint32_t total_t, uint32_t h,
+    uint32_t n_rows) {
+  const uint32_t i = blockIdx.x * NT + threadIdx.x;
+  const uint32_t rh = i / DV4;  // token * h + head
+  if (rh >= n_rows) return;
+  const uint32_t c4 = i % DV4;
+  const uint32_t t = rh / h;
+  const uint32_t hh = rh - t * h;
+  const int64_t li = (int64_t)hh * total_t + t;
+  float lp[S];
+  float m = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < S; ++p) {
+    lp[p] = part_lse[p * pl + li];
+    m = fmaxf(m, lp[p]);
+  }
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  if (m != -INFINITY) {
+#pragma unroll
+    for (int p = 0; p < S; ++p) {
+      const float w = lp[p] == -INFINITY ? 0.f : __expf(lp[p] - m);
+      const float4 o = reinterpret_cast<const float4*>(part_out + p * po)[i];
+      acc.x += w * o.x;
+      acc.y += w * o.y;
+      acc.z += w * o.z;
+      acc.w += w * o.w;
+      den += w;
+    }
+    const float inv = 1.f / den;
+    acc.x *= inv;
+    acc.y *= inv;
+    acc.z *= inv;
+    acc.w *= inv;
+  }
+  if (out_bf16) {
+    ushort4 b;
+    b.x = f32_to_bf16_rne(acc.x);
+    b.y = f32_to_bf16_rne(acc.y);
+    b.z = f32_to_bf16_rne(acc.z);
+    b.w = f32_to_bf16_rne(acc.w);
+    reinterpret_cast<ushort4*>(out)[i] = b;
+  } else {
+    reinterpret_cast<float4*>(out)[i] = acc;
+  }
+  if (c4 == 0) lse[li] = m == -INFINITY ? -INFINITY : m + __logf(den);
+}
+
 unsigned grid_for(int64_t work, int64_t per_block, unsigned cap) {
   int64_t g = (work + per_block - 1) / per_block;
   if (g < 1) g = 1;
@@ -360,9 +415,28 @@ hipError_t launch_split_combine(const float* part_out, const float* part_lse, in
   if (n <= 0) return hipSuccess;
   if (split < 1 || (dv % 4) || part_out_stride < n * 4 || part_lse_stride < (int64_t)total_t * h)
     return hipErrorInvalidValue;
+  const int bf = out_dtype == RA_BF16 ? 1 : 0;
+  const int64_t rows = (int64_t)total_t * h;
+  const unsigned blocks = (unsigned)((n + NT - 1) / NT);
+#define RA_COMBINE_FIXED(S, DV4)                                                                \
+  if (split == S && dv / 4 == DV4) {                                                           \
+    hipLaunchKernelGGL((split_combine_fixed_kernel<S, DV4>), dim3(blocks), dim3(NT), 0, st,    \
+                       part_out, part_lse, part_out_stride, part_lse_stride, out, bf, lse,     \
+                       (uint32_t)total_t, (uint32_t)h, (uint32_t)rows);                        \
+    return hipGetLastError();                                                                  \
+  }
+  if (n < ((int64_t)1 << 31)) {
+    RA_COMBINE_FIXED(2, 32)
+    RA_COMBINE_FIXED(4, 32)
+    RA_COMBINE_FIXED(8, 32)
+    RA_COMBINE_FIXED(2, 16)
+    RA_COMBINE_FIXED(4, 16)
+    RA_COMBINE_FIXED(8, 16)
+  }
+#undef RA_COMBINE_FIXED
   hipLaunchKernelGGL(split_combine_kernel, dim3(grid_for(n, NT, 8192u)), dim3(NT), 0, st,
-                     part_out, part_lse, split, part_out_stride, part_lse_stride, out,
-                     out_dtype == RA_BF16 ? 1 : 0, lse, total_t, h, dv / 4, n);
+                     part_out, part_lse, split, part_out_stride, part_lse_stride, out, bf, lse,
+                     total_t, h, dv / 4, n);
   return hipGetLastError();
 }
 
