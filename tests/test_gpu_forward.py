@@ -403,11 +403,12 @@ def _full_parity(w, fuse_modes=(0, 1, 2), determinism=False):
     return prob
 
 
-@pytest.mark.parametrize("split", ["1", "3", "8", "16"])
+@pytest.mark.parametrize("split", ["1", "2", "3", "4", "8", "16"])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_fused_rank_share_kv_split(split, out_dtype, monkeypatch):
     """A fused rank share whose key tiles are dealt over `split` parts (each
-    a float32 partial), combined by lse weight; with 16 parts some
+    a float32 partial), combined by lse weight (2, 4 and 8 parts by the
+    fixed-shape combine, 3 and 16 by the generic one); with 16 parts some
     workgroups of the first-half rows get no tile at all."""
     monkeypatch.setenv("RA_FWD_KV_SPLIT", split)
     w = synth.reduced("gqa_32k", 4096, 8)
