@@ -12,10 +12,10 @@
 //
 // dK/dV kernel -- workgroup = 128 keys of one kv head (4 waves x 32 keys).
 //   K and (at d_qk = 128) V of the wave's keys stay in registers, V
-//   otherwise in LDS (loaded once); the loop walks every
-//   query head of the kv group and every 32-row query tile of the segment
-//   part (causal: only tiles at or below the keys).  Per tile, with lane l
-//   owning key column l%32 of the 32x32 accumulators:
+//   otherwise in LDS (loaded once); the loop walks every query head of the
+//   kv group and every 32-row query tile of the segment part (causal: only
+//   tiles at or below the keys).  Per tile, with lane l owning key column
+//   l%32 of the 32x32 accumulators:
 //     S  = Q K^T, dP = dO V^T        A = Q / dO rows from LDS, B = K / V
 //                                    in registers (V in LDS at d_qk = 192)
 //     dV += P^T dO, dK += dS^T Q     A = P^T / dS^T straight from the S / dP
@@ -38,7 +38,10 @@
 // stage the prefetch.  The lse and delta of a query tile come along (4 bytes
 // per lane).  Each kernel runs one wave per SIMD (large accumulators), so
 // the LDS operand reads of a block of products are scheduled a few products
-// ahead (pipeline_lds_mfma).
+// ahead (pipeline_lds_mfma).  Only tiles that cross a part end or the
+// diagonal evaluate the mask, on a branch of their own.  At d_qk = 128 the
+// dQ kernel issues the softmax of one 32-key half between products it does
+// not feed (pipeline_lds_mfma_valu).
 
 #include <cstring>
 
