@@ -422,9 +422,10 @@ ra_status ra_segments_work(const ra_segment* segs, int32_t n_seg, int32_t hq,
  * tiles over all query heads and real rows carry at least 3/4 of the tiled
  * rows' work, each segment's rows weighted by its key count (so padding in
  * the tiles of short segments counts little), "attn_fwd_bf16" (4 waves,
- * 128-row tiles) otherwise, "attn_fwd_f32" for float32.  Both bf16 kernels compute the same result.  The environment
- * variable RA_FWD_KERNEL=pp or =4w forces one.  Host only; NULL (with
- * ra_last_error set) for an invalid descriptor.
+ * 128-row tiles) otherwise, "attn_fwd_f32" for float32.  Both bf16 kernels
+ * compute the same result.  The environment variable RA_FWD_KERNEL=pp or
+ * =4w forces one.  Host only; NULL (with ra_last_error set) for an invalid
+ * descriptor.
  */
 const char* ra_forward_kernel(const ra_attn_desc* d, ra_part q_part);
 
