@@ -621,8 +621,9 @@ def per_block_pass(a, w, prob, work, fl_pair, torch, L):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only: every simulated rank's "
-                                   "share runs in turn on a single MI355X; run with --gpus 1"}))
+        print(json.dumps({"error": "bench.py measures one GPU: every rank's share runs in turn "
+                                   "on a single MI355X (the ring's KV exchange is not timed); "
+                                   "run with --gpus 1"}))
         sys.exit(2)
     if a.copy_calibration_mib:
         copy_calibration(a.copy_calibration_mib)
