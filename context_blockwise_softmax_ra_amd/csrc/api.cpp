@@ -930,18 +930,16 @@ static ra_status rank_bwd_step(const ra_rank_bwd_desc* d, int s, ra_attn_desc* s
 
 // Rank-fused backward: one dK/dV launch over every owner's key tiles and
 // one dQ launch whose query tiles walk all owners' blocks, instead of one
-// pair of launches per ring step.  It pays where the per-step launches are
-// small or cut into many documents: packed documents, or shares of at most
-// 64K (row, head) pairs (8K MHA 206 -> 231, 128K varlen 128 -> 148 TFLOP/s
-// on one box).  Large single-sequence shares keep the per-step launches,
-// whose workgroups stream the same Q/dO (or K/V) tiles in step through the
-// L2 (32K GQA 483 vs 382, 256K MLA 569 vs 438 fused).
-// RA_BWD_RANK_FUSED=0 / =1 in the environment forces one form.
-static bool bwd_rank_fused(const ra_attn_desc& L, const Checked& c) {
+// pair of launches per ring step.  With the dK/dV launch ordered by kv head
+// (each XCD's workgroups share that head's Q/dO tiles in its L2) it is the
+// faster form on every workload: 8K MHA 306 vs 217 TFLOP/s, 128K varlen 197
+// vs 140, 32K GQA 610 vs 597, 256K MLA 660 vs 641 (same box, alternating).
+// It also needs no per-step partials: its workspace is delta and, on shares
+// with few query tiles, the dQ key-split partials.
+// RA_BWD_RANK_FUSED=0 in the environment selects the per-step form.
+static bool bwd_rank_fused() {
   const char* e = std::getenv("RA_BWD_RANK_FUSED");
-  if (e && !std::strcmp(e, "0")) return false;
-  if (e && !std::strcmp(e, "1")) return true;
-  return L.n_seq > 1 || (long long)c.total_q * L.hq <= 65536;
+  return !(e && !std::strcmp(e, "0"));
 }
 
 // dQ key split of the rank-fused backward: the walk's key tiles of a query
@@ -969,7 +967,7 @@ ra_status ra_rank_backward_workspace(const ra_rank_bwd_desc* d, size_t* bytes) {
   ra_status st = check_rank_common(d->local, d->cp_size, d->rank, d->k_blocks, d->v_blocks, &c);
   if (st != RA_OK) return st;
   const size_t delta_b = align256((size_t)c.total_q * d->local.hq * sizeof(float));
-  if (bwd_rank_fused(d->local, c)) {
+  if (bwd_rank_fused()) {
     const size_t part = align256((size_t)c.total_q * d->local.hq * d->local.dqk * sizeof(float));
     *bytes = delta_b + (size_t)(bwd_rank_ksplit(d->local, c) - 1) * part;
     return ok();
@@ -1026,7 +1024,7 @@ ra_status ra_rank_backward(const ra_rank_bwd_desc* d, void* stream) {
   const size_t delta_b = align256((size_t)c.total_q * L.hq * sizeof(float));
   float* part = reinterpret_cast<float*>(static_cast<char*>(d->workspace) + delta_b);
   hipError_t e;
-  if (bwd_rank_fused(L, c)) {
+  if (bwd_rank_fused()) {
     if (d->cp_size > ra::kMaxCp)
       return fail(RA_ERR_UNSUPPORTED, "rank-fused backward supports cp_size <= %d", ra::kMaxCp);
     ra::RankKV rk;

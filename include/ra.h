@@ -279,30 +279,29 @@ ra_status ra_block_attn_bwd(const ra_attn_desc* d, const void* dout, const float
  * output (out_dtype), lse the final lse; delta is computed into the
  * workspace.  dq [total_q, hq, dqk] float32 is added to.
  *
- * The workspace (device, caller-owned, ra_rank_backward_workspace bytes;
- * the same size for every rank of the ring) holds delta [hq, total_q] and
- * the dK/dV partials of the query split: on blocks with few 128-key tiles,
- * and on the causal diagonal block, up to 4 workgroups share a key tile,
- * each taking a contiguous share of its query iterations; share 0 adds into
- * the owner's dK/dV, shares 1.. store float32 partials in the workspace,
- * and a reduction adds them in share order (deterministic).  Likewise, on
+ * The share runs rank-fused: one dK/dV launch over the key tiles of every
+ * owner's block (each with that step's rule, added into that owner's
+ * dK/dV) and one dQ launch whose query tiles walk the key tiles of all
+ * blocks in ring order, dQ kept in registers; on shares with few query
+ * tiles up to 4 workgroups deal a query tile's walk, their float32 partials
+ * (after delta in the workspace) added in share order.
+ *
+ * RA_BWD_RANK_FUSED=0 in the environment selects the per-step form
+ * instead: one dK/dV and one dQ launch per ring step.  On blocks with few
+ * 128-key tiles, and on the causal diagonal block, up to 4 workgroups then
+ * share a key tile, each taking a contiguous share of its query iterations;
+ * share 0 adds into the owner's dK/dV, shares 1.. store float32 partials in
+ * the workspace, and a reduction adds them in share order.  Likewise, on
  * blocks with few 128-row query tiles, up to 4 workgroups share a query
  * tile for dQ, dealing its key tiles; share 0 adds into dq, the others'
- * float32 partials follow the dK/dV ones in the workspace.  A workspace
- * smaller than that size is rejected with RA_ERR_INVALID_ARG before any
- * launch.
+ * float32 partials follow the dK/dV ones in the workspace.
  *
- * That is the per-step form.  For packed documents (n_seq > 1) and for
- * shares of at most 64K (row, head) pairs the share runs rank-fused
- * instead: one dK/dV launch over the key tiles of every owner's block
- * (each with that step's rule, added into that owner's dK/dV) and one dQ
- * launch whose query tiles walk the key tiles of all blocks in ring order,
- * dQ kept in registers; on shares with few query tiles up to 4 workgroups
- * deal a query tile's walk, their float32 partials (after delta in the
- * workspace) added in share order.  The results are the same up to
- * rounding order; both forms are deterministic.  RA_BWD_RANK_FUSED=0 / =1
- * in the environment forces one form; ra_rank_backward_workspace reports
- * the size of the form that will run.
+ * Both forms are deterministic (no atomics; partials added in a fixed
+ * order) and give the same results up to rounding order.  The workspace
+ * (device, caller-owned, ra_rank_backward_workspace bytes for the form that
+ * will run; the same size for every rank of the ring) holds delta
+ * [hq, total_q] and those partials; a smaller one is rejected with
+ * RA_ERR_INVALID_ARG before any launch.
  * events (optional): host array of 2*cp_size hipEvent_t; events[0] is
  * recorded before the rank's first launch and events[2*cp_size-1] after its
  * last in both forms; the per-step form also records events[2s] / [2s+1]

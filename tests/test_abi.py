@@ -313,13 +313,12 @@ def test_rank_fused_backward_workspace_sizes(T, hq, hkv, C, ksplit_env, n_parts,
     assert sizes == {hq * T * 4 + n_parts * T * hq * 128 * 4}
 
 
-@pytest.mark.parametrize("name,fused", [("mha_8k", True), ("varlen_128k", True),
-                                        ("gqa_32k", False), ("mla_256k", False)])
-def test_rank_backward_form_choice(name, fused, monkeypatch):
-    """Without RA_BWD_RANK_FUSED the rank backward is fused for packed
-    documents and for shares of at most 64K (row, head) pairs, and runs one
-    pair of launches per step otherwise; the workspace follows the form
-    (delta and the fused dQ partials, or delta and the per-step partials)."""
+@pytest.mark.parametrize("name", ["mha_8k", "varlen_128k", "gqa_32k", "mla_256k"])
+def test_rank_backward_form_choice(name, monkeypatch):
+    """Without RA_BWD_RANK_FUSED the rank backward runs rank-fused (one
+    dK/dV and one dQ launch for the whole share); RA_BWD_RANK_FUSED=0 selects
+    one pair of launches per step.  The workspace follows the form (delta and
+    the fused dQ partials, or delta and the per-step partials)."""
     w = synth.WORKLOADS[name]
     cu_local, _ = L.ra_zigzag_shard_map(w.cp, 0, w.cu_global())
     local = _desc(hq=w.hq, hkv=w.hkv, dqk=w.dqk, dv=w.dv, cu=cu_local)
@@ -337,7 +336,7 @@ def test_rank_backward_form_choice(name, fused, monkeypatch):
         n = ctypes.c_size_t(0)
         assert L.lib().ra_rank_backward_workspace(ctypes.byref(rd), ctypes.byref(n)) == 0
         sizes[env] = n.value
-    assert sizes[None] == sizes["1" if fused else "0"]
+    assert sizes[None] == sizes["1"]
 
 
 def test_rank_backward_rejects_short_workspace(monkeypatch):

@@ -203,7 +203,7 @@ def test_mla_backward_reduced_full_parity():
 
 # Forms of the rank backward: (RA_BWD_RANK_FUSED, RA_BWD_QSPLIT,
 # RA_BWD_KV_SPLIT, RA_BWD_KSPLIT); "auto" leaves the choice to the library
-# (fused for packed documents and small shares).  Rank-fused ("1"): one dK/dV
+# (rank-fused).  Rank-fused ("1"): one dK/dV
 # launch over every owner's key tiles and one dQ launch walking all blocks,
 # ksplit = workgroups sharing a dQ query tile.  Per step ("0"): one pair of
 # launches per ring step; qsplit = workgroups sharing a dK/dV key tile,

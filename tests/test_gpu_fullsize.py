@@ -87,14 +87,19 @@ def test_gqa_32k_rank_share_full_parity(gqa_32k, rank, monkeypatch):
     check_lse(to_np(lses[rank]), ref_l, f"rank{rank} lse (all rows)")
 
 
-def test_gqa_32k_backward_sampled_and_sum_rules(gqa_32k, monkeypatch):
-    """Full-size backward with the automatic splits: sampled dQ rows of
-    ranks 0, 3 and 7, dK/dV of the last 256 keys (seen only by the last 256
-    rows, which rank 0 holds), and the sum rules over every key."""
+@pytest.mark.parametrize("fused", [True, False], ids=["rank_fused", "per_step"])
+def test_gqa_32k_backward_sampled_and_sum_rules(fused, gqa_32k, monkeypatch):
+    """Full-size backward in both forms with their automatic splits: sampled
+    dQ rows of ranks 0, 3 and 7, dK/dV of the last 256 keys (seen only by
+    the last 256 rows, which rank 0 holds), and the sum rules over every
+    key."""
     for v in ("RA_BWD_RANK_FUSED", "RA_BWD_QSPLIT", "RA_BWD_KSPLIT", "RA_BWD_KV_SPLIT"):
         monkeypatch.delenv(v, raising=False)
+    if not fused:
+        monkeypatch.setenv("RA_BWD_RANK_FUSED", "0")
     w, prob, (q64, k64, v64, do64) = gqa_32k
-    log(f"gqa_32k backward (full size): S={w.seqlen} C={w.cp}")
+    log(f"gqa_32k backward (full size, {'rank-fused' if fused else 'per step'}): "
+        f"S={w.seqlen} C={w.cp}")
     _, _, dqs, dks, dvs = _backward_all(prob)
     cu = w.cu_global()
     lay = oracle.ref.Layout(cu)
@@ -186,5 +191,6 @@ def test_mla_16k_cp32_forward_full_parity(monkeypatch):
         check_lse(to_np(lses[r]), rl[:, rows], f"rank{r} lse")
 
 
-def test_mla_16k_cp32_backward_full_parity(monkeypatch):
-    _full_backward(_mla_mini(), monkeypatch)
+@pytest.mark.parametrize("fused", [True, False], ids=["rank_fused", "per_step"])
+def test_mla_16k_cp32_backward_full_parity(fused, monkeypatch):
+    _full_backward(_mla_mini(), monkeypatch, fused)
