@@ -946,10 +946,19 @@ static bool bwd_rank_fused() {
 // tile dealt over up to kMaxQsplit workgroups, doubled until the launch has
 // 256 workgroups (the dK/dV launch over all owners is large enough alone).
 // RA_BWD_KSPLIT=n in the environment forces n.
+// 128-row query tiles of the local rows, segment by segment
+static long long rank_q_tiles(const ra_attn_desc& L) {
+  long long t = 0;
+  for (int s = 0; s < L.n_seq; ++s)
+    t += (L.cu_seqlens_q_host[s + 1] - L.cu_seqlens_q_host[s] + 127) / 128;
+  return t;
+}
+
 static int bwd_rank_ksplit(const ra_attn_desc& L, const Checked& c) {
+  (void)c;
   const char* e = std::getenv("RA_BWD_KSPLIT");
   if (e && *e) return std::max(1, std::min(std::atoi(e), kMaxQsplit));
-  const long long wg = (long long)L.n_seq * L.hq * ((c.max_q_part + 127) / 128);
+  const long long wg = rank_q_tiles(L) * L.hq;
   int n = 1;
   while (n < kMaxQsplit && wg * n < 256) n *= 2;
   return n;
@@ -1039,6 +1048,26 @@ ra_status ra_rank_backward(const ra_rank_bwd_desc* d, void* stream) {
       rg.dk[j] = d->dk_blocks[j];
       rg.dv[j] = d->dv_blocks[j];
     }
+    // live 128-key tiles of each step's block (the dK/dV grid per kv head)
+    long long kv_tiles = 0;
+    for (int o = 0; o < d->cp_size; ++o) {
+      rk.kv_tile_off[o] = (int32_t)kv_tiles;
+      int causal, qp, kp;
+      ra::owner_plan(d->rank, (d->rank - o + d->cp_size) % d->cp_size, &causal, &qp, &kp);
+      for (int s = 0; s < L.n_seq; ++s) {
+        int ql, qh, kl, kh;
+        ra::part_range(L.cu_seqlens_q_host[s], L.cu_seqlens_q_host[s + 1], qp, &ql, &qh);
+        ra::part_range(L.cu_seqlens_k_host[s], L.cu_seqlens_k_host[s + 1], kp, &kl, &kh);
+        if (qh > ql && kh > kl) kv_tiles += (kh - kl + 127) / 128;
+      }
+      if (kv_tiles * L.hkv > 0x7fffffffLL)
+        return fail(RA_ERR_UNSUPPORTED, "rank-fused backward: too many key tiles");
+    }
+    rk.kv_tile_off[d->cp_size] = (int32_t)kv_tiles;
+    const long long q_tiles = rank_q_tiles(L);
+    if (q_tiles * L.hq * kMaxQsplit > 0x7fffffffLL)
+      return fail(RA_ERR_UNSUPPORTED, "rank-fused backward: too many query tiles");
+    rk.q_tiles = (int32_t)q_tiles;
     ra_attn_desc sd = L;
     sd.k = d->k_blocks[0];
     sd.v = d->v_blocks[0];

@@ -89,6 +89,45 @@ struct GeoKV {
   static_assert(DV == 128, "dO rows are 256 bytes");
 };
 
+// Tile r (0-based) of the live 128-key (BY_KEYS) or 128-row tiles of a
+// block, counted segment by segment in the rank-fused grids: a segment
+// contributes ceil(length / 128) tiles along that axis if some row of its
+// query part sees some key of its key part.  Each wave scans 64 segments
+// at a time (prefix sum over lanes, then the first lane past r); the
+// results are the same in every lane: the segment, the tile's index in it
+// and the segment's tile count.  Returns false if r is past the last tile.
+template <bool BY_KEYS>
+__device__ __forceinline__ bool locate_tile(const int32_t* cu_q, const int32_t* cu_k, int n_seq,
+                                            int qp, int kp, int r, int* seg, int* idx, int* cnt) {
+  const int lane = threadIdx.x & 63;
+  for (int base = 0; base < n_seq; base += 64) {
+    const int s = base + lane;
+    int t = 0;
+    if (s < n_seq) {
+      int ql, qh, kl, kh;
+      part_range(cu_q[s], cu_q[s + 1], qp, &ql, &qh);
+      part_range(cu_k[s], cu_k[s + 1], kp, &kl, &kh);
+      t = (qh > ql && kh > kl) ? ((BY_KEYS ? kh - kl : qh - ql) + 127) / 128 : 0;
+    }
+    int inc = t;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int u = __shfl_up(inc, d, 64);
+      if (lane >= d) inc += u;
+    }
+    const unsigned long long hit = __ballot(inc > r);
+    if (hit) {
+      const int f = __builtin_ctzll(hit);
+      *seg = __builtin_amdgcn_readfirstlane(base + f);
+      *idx = __builtin_amdgcn_readfirstlane(r - __shfl(inc - t, f, 64));
+      *cnt = __builtin_amdgcn_readfirstlane(__shfl(t, f, 64));
+      return true;
+    }
+    r = __builtin_amdgcn_readfirstlane(r - __shfl(inc, 63, 64));
+  }
+  return false;
+}
+
 // QS ("query split"): a workgroup covers 32 keys and its 4 waves split the
 // (query head, query tile) iterations among themselves, each with its own
 // two LDS stages and no barrier in the loop; the waves' dK/dV are added in
@@ -129,25 +168,35 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a, RankKV
   // documents: they all read that head's Q and dO tiles, which then stay in
   // the XCD's L2 (dealt over the XCDs, every L2 fetched every head's tiles;
   // 32K GQA backward 478 -> 284 TFLOP/s).  The diagonal block comes first.
+  // A rank share's grid holds only live tiles: per kv head, the ring steps
+  // in order, each with its owner's live tiles segment by segment.
   int b = (!RANK && a.n_seq > 1) ? xcd_deal(blockIdx.x, gridDim.x, nsp)
                                  : xcd_remap(blockIdx.x, gridDim.x);
   const int sp = b % nsp;
   b /= nsp;
-  const int kt = b % a.n_ktiles;
-  b /= a.n_ktiles;
-  int kvh, seg, step_o = 0;
+  int kt, kvh, seg, step_o = 0;
+  int own_causal = CAUSAL ? 1 : 0, own_qp = a.q_part, own_kp = a.k_part;
   if (RANK) {
-    seg = b % a.n_seq;
-    b /= a.n_seq;
-    step_o = b % rk.cp;
-    kvh = b / rk.cp;
+    const int per_head = rk.kv_tile_off[rk.cp];
+    kvh = b / per_head;
+    int r = b - kvh * per_head;
+    while (step_o + 1 < rk.cp && r >= rk.kv_tile_off[step_o + 1]) ++step_o;
+    r -= rk.kv_tile_off[step_o];
+    owner_plan(rk.rank, (rk.rank - step_o + rk.cp) % rk.cp, &own_causal, &own_qp, &own_kp);
+    if (a.n_seq == 1) {
+      seg = 0;
+      kt = r;
+    } else {
+      int cnt;
+      if (!locate_tile<true>(a.cu_q, a.cu_k, a.n_seq, own_qp, own_kp, r, &seg, &kt, &cnt)) return;
+    }
   } else {
+    kt = b % a.n_ktiles;
+    b /= a.n_ktiles;
     kvh = b % a.hkv;
     seg = b / a.hkv;
   }
   const int owner = RANK ? (rk.rank - step_o + rk.cp) % rk.cp : 0;
-  int own_causal = CAUSAL ? 1 : 0, own_qp = a.q_part, own_kp = a.k_part;
-  if (RANK) owner_plan(rk.rank, owner, &own_causal, &own_qp, &own_kp);
   const bool causal = RANK ? own_causal != 0 : CAUSAL;
   const void* kptr = RANK ? rk.k[owner] : a.k;
   const void* vptr = RANK ? rk.v[owner] : a.v;
@@ -548,17 +597,29 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a, RankKV r
   b /= nks;
   const int hg = b % a.group;
   b /= a.group;
-  const int qt_rev = b % a.n_qtiles;
-  b /= a.n_qtiles;
-  int kvh, seg;
+  int kvh, seg, qt;
   if (RANK) {
-    seg = b % a.n_seq;
-    kvh = b / a.n_seq;
+    // only live tiles: per kv head, each segment's query tiles, the
+    // heaviest (last rows) first
+    kvh = b / rk.q_tiles;
+    const int r = b - kvh * rk.q_tiles;
+    int idx, cnt;
+    if (a.n_seq == 1) {
+      seg = 0;
+      idx = r;
+      cnt = a.n_qtiles;
+    } else if (!locate_tile<false>(a.cu_q, a.cu_k, a.n_seq, RA_PART_ALL, RA_PART_ALL, r, &seg,
+                                   &idx, &cnt)) {
+      return;
+    }
+    qt = cnt - 1 - idx;
   } else {
+    const int qt_rev = b % a.n_qtiles;
+    b /= a.n_qtiles;
     kvh = b % a.hkv;
     seg = b / a.hkv;
+    qt = CAUSAL ? (a.n_qtiles - 1 - qt_rev) : qt_rev;  // heaviest first
   }
-  const int qt = (CAUSAL || RANK) ? (a.n_qtiles - 1 - qt_rev) : qt_rev;  // heaviest first
   const int h = kvh * a.group + hg;
 
   int q_lo, q_hi;
@@ -947,15 +1008,16 @@ hipError_t launch_attn_bwd_bf16(const AttnArgs& a0, int dqk, int dv, bool causal
 
 hipError_t launch_rank_bwd_bf16(const AttnArgs& a0, const RankKV& rk, const RankGrad& rg, int dqk,
                                 int dv, hipStream_t st) {
-  // a0.n_qtiles counts 128-row query tiles of the local rows, a0.n_ktiles
-  // 128-key tiles of a whole local segment (the largest part of any owner)
+  // the dQ grid is kv heads x rk.q_tiles live 128-row query tiles x group x
+  // key shares, the dK/dV grid kv heads x rk.kv_tile_off[rk.cp] live
+  // 128-key tiles
   AttnArgs a = a0;
   a.q_part = RA_PART_ALL;
   a.k_part = RA_PART_ALL;
   a.qsplit = 1;
   if (a.ksplit < 1 || !a.dq_part) a.ksplit = 1;
-  const long long nq = (long long)a.n_seq * a.hkv * a.n_qtiles * a.group * a.ksplit;
-  const long long nk = (long long)rk.cp * a.n_seq * a.hkv * a.n_ktiles;
+  const long long nq = (long long)a.hkv * rk.q_tiles * a.group * a.ksplit;
+  const long long nk = (long long)a.hkv * rk.kv_tile_off[rk.cp];
   if (nq > 0x7fffffffLL || nk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (dqk == 128 && dv == 128) {
     if (nk > 0)

@@ -79,6 +79,14 @@ struct RankKV {
   // out + p * part_out_stride, lse + p * part_lse_stride (elements)
   int32_t split;
   int64_t part_out_stride, part_lse_stride;
+  // rank-fused dK/dV launch: kv_tile_off[o] counts the 128-key tiles (with
+  // a row that sees them) of the owners of ring steps before o, over all
+  // segments; kv_tile_off[cp] tiles per kv head make up the grid, so no
+  // workgroup lands past a short segment's keys
+  int32_t kv_tile_off[kMaxCp + 1];
+  // rank-fused dQ launch: 128-row query tiles of the local rows, segment by
+  // segment (the grid per kv head, times the group and the key shares)
+  int32_t q_tiles;
 };
 
 // dK / dV accumulators of every owner for a rank's fused backward (one

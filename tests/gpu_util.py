@@ -71,9 +71,11 @@ def global_inputs(w: synth.Workload, with_dout: bool = False):
     return (q, k, v, do)
 
 
-def make_problem(w: synth.Workload, with_dout=False, device="cuda:0"):
+def make_problem(w: synth.Workload, with_dout=False, device="cuda:0", dout_scale=1.0):
     from context_blockwise_softmax_ra_amd.ring import RingProblem
     q, k, v, do = global_inputs(w, with_dout)
+    if do is not None and dout_scale != 1.0:
+        do = do * dout_scale
     dev = torch.device(device)
     prob = RingProblem(q.to(dev), k.to(dev), v.to(dev), w.cu_global(), w.cp,
                        dout_glob=do.to(dev) if do is not None else None)
