@@ -580,8 +580,12 @@ static int fwd_kv_split(const ra_rank_desc* d, const Checked& c) {
   if (use_pingpong(&L, RA_PART_ALL)) return 1;
   const char* e = std::getenv("RA_FWD_KV_SPLIT");
   if (e && *e) return std::max(1, std::min(std::atoi(e), kMaxFwdSplit));
-  const long long wg = (long long)L.n_seq * L.hkv * (L.hq / L.hkv) *
-                       ((c.max_q_part + ra::kFwdBlockM - 1) / ra::kFwdBlockM);
+  (void)c;
+  long long tiles = 0;  // 128-row query tiles of all segments (the launch's grid per head)
+  for (int s = 0; s < L.n_seq; ++s)
+    tiles += (L.cu_seqlens_q_host[s + 1] - L.cu_seqlens_q_host[s] + ra::kFwdBlockM - 1) /
+             ra::kFwdBlockM;
+  const long long wg = tiles * L.hq;
   if (wg <= 0) return 1;
   if (wg < 256) return (int)std::min<long long>(8, (512 + wg - 1) / wg);
   // Long shares of 1-4 workgroups per slot (two per CU): rows on average
@@ -637,6 +641,55 @@ ra_status ra_rank_forward_workspace(const ra_rank_desc* d, size_t* bytes) {
   if (!d->fuse_merge && d->cp_size > 1) b += out_b + lse_b;  // one partial
   *bytes = b;
   return ok();
+}
+
+// Query tiles (bm rows) of a packed rank share: their number, and (up to
+// kMaxTileOrder tiles) the order in which the launch takes them.
+// The work of a tile is estimated by the 64-key tiles it visits over the
+// ring's blocks (the kernel's block walk); heaviest first is the
+// longest-processing-time order, so a launch over many short documents and
+// a few long ones does not end on a long document's tiles.  The tile list
+// is segment by segment, each segment's heaviest (last) tile first.
+static ra_status order_packed_tiles(const ra_attn_desc& L, int C, int rank, int bm,
+                                     bool half_tiles, ra::RankKV* rk, int32_t* n_tiles) {
+  std::vector<std::pair<long long, int>> cost;  // (estimated work, tile)
+  long long n = 0;
+  for (int s = 0; s < L.n_seq; ++s) {
+    const int len = L.cu_seqlens_q_host[s + 1] - L.cu_seqlens_q_host[s], half = len / 2;
+    const int nh = half_tiles ? (half + bm - 1) / bm : 0;
+    const int nt = half_tiles ? nh + (len - half + bm - 1) / bm : (len + bm - 1) / bm;
+    for (int i = 0; i < nt; ++i, ++n) {
+      if (n >= ra::kMaxTileOrder) continue;
+      const int qt = nt - 1 - i;
+      long long q0 = (long long)qt * bm, t_hi = len;
+      if (half_tiles) {
+        if (qt < nh) t_hi = half;
+        else q0 = half + (long long)(qt - nh) * bm;
+      }
+      const long long last = std::min(q0 + bm, t_hi) - 1;
+      long long w = 0;
+      for (int o = 0; o < C; ++o) {
+        const int owner = (rank - o + C) % C;
+        long long kend;
+        if (o == 0) kend = std::min<long long>(len, last + 1);
+        else if (owner < rank) kend = half;
+        else kend = last >= half ? len : 0;
+        w += (kend + 63) / 64;
+      }
+      cost.emplace_back(w, (int)n);
+    }
+  }
+  if (n * L.hq > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "too many query tiles");
+  *n_tiles = (int32_t)n;
+  rk->tile_ordered = n <= ra::kMaxTileOrder;
+  if (rk->tile_ordered) {
+    std::stable_sort(cost.begin(), cost.end(),
+                     [](const std::pair<long long, int>& x, const std::pair<long long, int>& y) {
+                       return x.first > y.first;
+                     });
+    for (int u = 0; u < (int)n; ++u) rk->tile_order[u] = (uint16_t)cost[u].second;
+  }
+  return RA_OK;
 }
 
 ra_status ra_rank_forward(const ra_rank_desc* d, void* stream) {
@@ -707,6 +760,10 @@ ra_status ra_rank_forward(const ra_rank_desc* d, void* stream) {
       a.half_tiles = 1;
       a.n_qtiles_half = nh;
     }
+    if (L.n_seq > 1 &&
+        (st = order_packed_tiles(L, d->cp_size, d->rank, pp ? 256 : ra::kFwdBlockM,
+                                 a.half_tiles != 0, &rk, &rk.fwd_tiles)) != RA_OK)
+      return st;
     if (d->events && d->events[0] &&
         (e = hipEventRecord((hipEvent_t)d->events[0], hs)) != hipSuccess)
       return hip_fail(e, "event record");
@@ -1068,6 +1125,10 @@ ra_status ra_rank_backward(const ra_rank_bwd_desc* d, void* stream) {
     if (q_tiles * L.hq * kMaxQsplit > 0x7fffffffLL)
       return fail(RA_ERR_UNSUPPORTED, "rank-fused backward: too many query tiles");
     rk.q_tiles = (int32_t)q_tiles;
+    // the dQ tiles walk the blocks as the forward's do: same heaviest-first order
+    if (L.n_seq > 1 && (st = order_packed_tiles(L, d->cp_size, d->rank, 128, false, &rk,
+                                                &rk.q_tiles)) != RA_OK)
+      return st;
     ra_attn_desc sd = L;
     sd.k = d->k_blocks[0];
     sd.v = d->v_blocks[0];

@@ -89,43 +89,19 @@ struct GeoKV {
   static_assert(DV == 128, "dO rows are 256 bytes");
 };
 
-// Tile r (0-based) of the live 128-key (BY_KEYS) or 128-row tiles of a
-// block, counted segment by segment in the rank-fused grids: a segment
-// contributes ceil(length / 128) tiles along that axis if some row of its
-// query part sees some key of its key part.  Each wave scans 64 segments
-// at a time (prefix sum over lanes, then the first lane past r); the
-// results are the same in every lane: the segment, the tile's index in it
-// and the segment's tile count.  Returns false if r is past the last tile.
+// Tile r of the live 128-key (BY_KEYS) or 128-row tiles of a block in the
+// rank-fused grids: a segment contributes ceil(length / 128) tiles along
+// that axis if some row of its query part sees some key of its key part.
 template <bool BY_KEYS>
 __device__ __forceinline__ bool locate_tile(const int32_t* cu_q, const int32_t* cu_k, int n_seq,
                                             int qp, int kp, int r, int* seg, int* idx, int* cnt) {
-  const int lane = threadIdx.x & 63;
-  for (int base = 0; base < n_seq; base += 64) {
-    const int s = base + lane;
-    int t = 0;
-    if (s < n_seq) {
-      int ql, qh, kl, kh;
-      part_range(cu_q[s], cu_q[s + 1], qp, &ql, &qh);
-      part_range(cu_k[s], cu_k[s + 1], kp, &kl, &kh);
-      t = (qh > ql && kh > kl) ? ((BY_KEYS ? kh - kl : qh - ql) + 127) / 128 : 0;
-    }
-    int inc = t;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int u = __shfl_up(inc, d, 64);
-      if (lane >= d) inc += u;
-    }
-    const unsigned long long hit = __ballot(inc > r);
-    if (hit) {
-      const int f = __builtin_ctzll(hit);
-      *seg = __builtin_amdgcn_readfirstlane(base + f);
-      *idx = __builtin_amdgcn_readfirstlane(r - __shfl(inc - t, f, 64));
-      *cnt = __builtin_amdgcn_readfirstlane(__shfl(t, f, 64));
-      return true;
-    }
-    r = __builtin_amdgcn_readfirstlane(r - __shfl(inc, 63, 64));
-  }
-  return false;
+  auto count = [&](int s) {
+    int ql, qh, kl, kh;
+    part_range(cu_q[s], cu_q[s + 1], qp, &ql, &qh);
+    part_range(cu_k[s], cu_k[s + 1], kp, &kl, &kh);
+    return (qh > ql && kh > kl) ? ((BY_KEYS ? kh - kl : qh - ql) + 127) / 128 : 0;
+  };
+  return locate_in_segments(n_seq, r, count, seg, idx, cnt);
 }
 
 // QS ("query split"): a workgroup covers 32 keys and its 4 waves split the
@@ -600,7 +576,8 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a, RankKV r
   int kvh, seg, qt;
   if (RANK) {
     // only live tiles: per kv head, each segment's query tiles, the
-    // heaviest (last rows) first
+    // heaviest (last rows) first; packed segments in the host's
+    // heaviest-first order of those tiles
     kvh = b / rk.q_tiles;
     const int r = b - kvh * rk.q_tiles;
     int idx, cnt;
@@ -608,8 +585,9 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a, RankKV r
       seg = 0;
       idx = r;
       cnt = a.n_qtiles;
-    } else if (!locate_tile<false>(a.cu_q, a.cu_k, a.n_seq, RA_PART_ALL, RA_PART_ALL, r, &seg,
-                                   &idx, &cnt)) {
+    } else if (!locate_tile<false>(a.cu_q, a.cu_k, a.n_seq, RA_PART_ALL, RA_PART_ALL,
+                                   rk.tile_ordered ? (int)rk.tile_order[r] : r, &seg, &idx,
+                                   &cnt)) {
       return;
     }
     qt = cnt - 1 - idx;

@@ -83,15 +83,31 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
   int b = causal_only ? xcd_deal(blockIdx.x, nb, group) : xcd_remap(blockIdx.x, nb);
   const int hg = b % group;
   b /= group;
-  const int qt_rev = b % a.n_qtiles;
-  b /= a.n_qtiles;
-  const int kvh = b % a.hkv;
-  b /= a.hkv;
-  const int seg = MODE == 2 ? b % a.n_seq : b;
-  const int kv_part = MODE == 2 ? b / a.n_seq : 0;  // part of a KV-split rank share
-  // heaviest query tiles first (causal: later rows see more keys; rank share:
-  // second-half rows also see the blocks of later ranks)
-  const int qt = MODE != 0 ? (a.n_qtiles - 1 - qt_rev) : qt_rev;
+  int kvh, seg, kv_part = 0, qt;  // kv_part: part of a KV-split rank share
+  if (MODE == 2 && a.n_seq > 1) {
+    // packed documents: only live tiles, the kv heads of one tile together,
+    // tiles in the host's heaviest-first order (or segment by segment, each
+    // segment's heaviest tile first), parts slowest
+    kvh = b % a.hkv;
+    b /= a.hkv;
+    const int u = b % rk.fwd_tiles;
+    kv_part = b / rk.fwd_tiles;
+    const int j = rk.tile_ordered ? (int)rk.tile_order[u] : u;
+    auto count = [&](int s) { return (a.cu_q[s + 1] - a.cu_q[s] + BM - 1) / BM; };
+    int idx, cnt;
+    if (!locate_in_segments(a.n_seq, j, count, &seg, &idx, &cnt)) return;
+    qt = cnt - 1 - idx;
+  } else {
+    const int qt_rev = b % a.n_qtiles;
+    b /= a.n_qtiles;
+    kvh = b % a.hkv;
+    b /= a.hkv;
+    seg = MODE == 2 ? b % a.n_seq : b;
+    kv_part = MODE == 2 ? b / a.n_seq : 0;
+    // heaviest query tiles first (causal: later rows see more keys; rank
+    // share: second-half rows also see the blocks of later ranks)
+    qt = MODE != 0 ? (a.n_qtiles - 1 - qt_rev) : qt_rev;
+  }
   const int h = kvh * group + hg;
 
   int q_lo, q_hi, kseg0, kseg1, seg_diag = 0;
@@ -442,7 +458,11 @@ hipError_t launch_t(const AttnArgs& a, const RankKV* rk, bool causal, bool merge
                     hipStream_t st) {
   const int split = rk ? max(rk->split, 1) : 1;
   if (rk && split > 1 && out_bf16) return hipErrorInvalidValue;  // parts are float32
-  const long long nblk = (long long)a.n_seq * a.hkv * a.n_qtiles * a.group * split;
+  // a packed rank share lists live tiles only (rk->fwd_tiles over all
+  // segments)
+  const long long nblk = (rk && a.n_seq > 1)
+                             ? (long long)rk->fwd_tiles * a.hkv * a.group * split
+                             : (long long)a.n_seq * a.hkv * a.n_qtiles * a.group * split;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)nblk), block(NT);

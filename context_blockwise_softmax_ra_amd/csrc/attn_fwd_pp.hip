@@ -96,11 +96,29 @@ __global__ __launch_bounds__(PT, 1) void attn_fwd_pp_kernel(AttnArgs a, RankKV r
   int b = causal_only ? xcd_deal(blockIdx.x, nb, group) : xcd_remap(blockIdx.x, nb);
   const int hg = b % group;
   b /= group;
-  const int qt_rev = b % n_qtiles;
-  b /= n_qtiles;
-  const int kvh = b % a.hkv;
-  const int seg = b / a.hkv;
-  const int qt = MODE != 0 ? (n_qtiles - 1 - qt_rev) : qt_rev;  // heaviest first
+  int kvh, seg, qt;
+  if (MODE == 2 && a.n_seq > 1) {
+    // packed documents: only live tiles, the kv heads of one tile
+    // together, tiles in the host's heaviest-first order (or segment by
+    // segment, each segment's heaviest tile first)
+    kvh = b % a.hkv;
+    const int u = b / a.hkv;
+    const int j = rk.tile_ordered ? (int)rk.tile_order[u] : u;
+    auto count = [&](int s) {
+      const int len = a.cu_q[s + 1] - a.cu_q[s], half = len >> 1;
+      return a.half_tiles ? (half + PBM - 1) / PBM + (len - half + PBM - 1) / PBM
+                          : (len + PBM - 1) / PBM;
+    };
+    int idx, cnt;
+    if (!locate_in_segments(a.n_seq, j, count, &seg, &idx, &cnt)) return;
+    qt = cnt - 1 - idx;
+  } else {
+    const int qt_rev = b % n_qtiles;
+    b /= n_qtiles;
+    kvh = b % a.hkv;
+    seg = b / a.hkv;
+    qt = MODE != 0 ? (n_qtiles - 1 - qt_rev) : qt_rev;  // heaviest first
+  }
   const int h = kvh * group + hg;
 
   int q_lo, q_hi;
@@ -451,7 +469,10 @@ hipError_t launch_pp_t(const AttnArgs& a, const RankKV* rk, bool causal, bool me
   // query tiles of 256 rows from the 128-row count the host computed, or
   // the host's count of half tiles
   const int nq = (rk && a.half_tiles) ? a.n_qtiles_half : (a.n_qtiles + 1) / 2;
-  const long long nblk = (long long)a.n_seq * a.hkv * nq * a.group;
+  // a packed rank share lists live tiles only (rk->fwd_tiles over all
+  // segments), the kv heads of one tile together
+  const long long nblk = (rk && a.n_seq > 1) ? (long long)rk->fwd_tiles * a.hkv * a.group
+                                             : (long long)a.n_seq * a.hkv * nq * a.group;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)nblk), block(PT);

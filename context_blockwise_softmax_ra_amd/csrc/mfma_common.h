@@ -74,6 +74,37 @@ __device__ __forceinline__ int sigma(int mm) {
   return ((i >> 3) << 4) | (g << 3) | (i & 7);
 }
 
+// Item r (0-based) of a list in which segment s = 0, 1, ... holds count(s)
+// items, for grids that list only the live tiles of packed segments.  Each
+// wave scans 64 segments at a time (a prefix sum over its lanes, then the
+// first lane past r); the results are wave-uniform: the segment, the item's
+// index in it and the segment's count.  Returns false if r is past the end.
+template <class Count>
+__device__ __forceinline__ bool locate_in_segments(int n_seq, int r, Count count, int* seg,
+                                                   int* idx, int* cnt) {
+  const int lane = threadIdx.x & 63;
+  for (int base = 0; base < n_seq; base += 64) {
+    const int s = base + lane;
+    const int t = s < n_seq ? count(s) : 0;
+    int inc = t;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int u = __shfl_up(inc, d, 64);
+      if (lane >= d) inc += u;
+    }
+    const unsigned long long hit = __ballot(inc > r);
+    if (hit) {
+      const int f = __builtin_ctzll(hit);
+      *seg = __builtin_amdgcn_readfirstlane(base + f);
+      *idx = __builtin_amdgcn_readfirstlane(r - __shfl(inc - t, f, 64));
+      *cnt = __builtin_amdgcn_readfirstlane(__shfl(t, f, 64));
+      return true;
+    }
+    r = __builtin_amdgcn_readfirstlane(r - __shfl(inc, 63, 64));
+  }
+  return false;
+}
+
 // Blocks are dispatched round-robin over the 8 XCDs (b % 8); give each XCD
 // a contiguous range of logical tiles so neighbours share its L2.
 __device__ __forceinline__ int xcd_remap(int b, int nb) {

@@ -70,6 +70,7 @@ struct AttnArgs {
 
 // KV blocks of every owner for a rank's fused forward (one launch per rank).
 constexpr int kMaxCp = 64;
+constexpr int kMaxTileOrder = 512;  // tiles a packed share can order (kernel arguments)
 struct RankKV {
   const void* k[kMaxCp];
   const void* v[kMaxCp];
@@ -85,8 +86,18 @@ struct RankKV {
   // workgroup lands past a short segment's keys
   int32_t kv_tile_off[kMaxCp + 1];
   // rank-fused dQ launch: 128-row query tiles of the local rows, segment by
-  // segment (the grid per kv head, times the group and the key shares)
+  // segment (the grid per kv head, times the group and the key shares);
+  // over packed segments taken in tile_order as the forward's tiles are
   int32_t q_tiles;
+  // rank-fused forward over packed segments: fwd_tiles query tiles (256
+  // rows on the ping-pong kernel, half tiles if AttnArgs::half_tiles; 128
+  // on the 4-wave kernel) of all segments, listed segment by segment with
+  // each segment's heaviest tile first; if tile_ordered, workgroup unit u
+  // (all kv heads of one tile) takes tile tile_order[u] of that list (the
+  // host's heaviest-first order), else tile u
+  int32_t fwd_tiles;
+  int32_t tile_ordered;
+  uint16_t tile_order[kMaxTileOrder];
 };
 
 // dK / dV accumulators of every owner for a rank's fused backward (one

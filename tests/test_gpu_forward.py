@@ -436,6 +436,19 @@ def test_varlen_workload_reduced_full_parity():
     _full_parity(w)
 
 
+@pytest.mark.parametrize("half", ["0", "1"])
+def test_many_documents_forward_parity(half, monkeypatch):
+    """161 packed documents (4..40 tokens and one of 576, CP = 2): the
+    fused share on the ping-pong kernel lists only live query tiles, located
+    by a scan of the segments 64 at a time (three passes here), with whole
+    and with half tiles; the 4-wave kernel alongside."""
+    monkeypatch.setenv("RA_FWD_HALF_TILES", half)
+    w = synth.reduced("varlen_128k", 4096, 2)
+    w.doc_lengths = [4 * (1 + i % 10) for i in range(160)] + [576]
+    assert sum(w.doc_lengths) == 4096 and len(w.doc_lengths) > 128
+    _full_parity(w, fuse_modes=(2,))
+
+
 def test_mla_forward_reduced_full_parity():
     _full_parity(synth.reduced("mla_256k", 4096, 8))
 
