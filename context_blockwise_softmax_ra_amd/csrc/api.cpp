@@ -1105,8 +1105,11 @@ ra_status ra_rank_backward(const ra_rank_bwd_desc* d, void* stream) {
       rg.dk[j] = d->dk_blocks[j];
       rg.dv[j] = d->dv_blocks[j];
     }
-    // live 128-key tiles of each step's block (the dK/dV grid per kv head)
+    // live 128-key tiles of each step's block (the dK/dV grid per kv head),
+    // with their work in 32-row query iterations (plus two for a
+    // workgroup's set-up and epilogue)
     long long kv_tiles = 0;
+    std::vector<std::pair<long long, int>> kv_cost;
     for (int o = 0; o < d->cp_size; ++o) {
       rk.kv_tile_off[o] = (int32_t)kv_tiles;
       int causal, qp, kp;
@@ -1115,19 +1118,40 @@ ra_status ra_rank_backward(const ra_rank_bwd_desc* d, void* stream) {
         int ql, qh, kl, kh;
         ra::part_range(L.cu_seqlens_q_host[s], L.cu_seqlens_q_host[s + 1], qp, &ql, &qh);
         ra::part_range(L.cu_seqlens_k_host[s], L.cu_seqlens_k_host[s + 1], kp, &kl, &kh);
-        if (qh > ql && kh > kl) kv_tiles += (kh - kl + 127) / 128;
+        if (qh <= ql || kh <= kl) continue;
+        const int nkt = (kh - kl + 127) / 128, nqt = (qh - ql + 31) / 32;
+        for (int kt = 0; kt < nkt && kv_tiles + kt < ra::kMaxTileOrder; ++kt)
+          kv_cost.emplace_back((long long)std::max(nqt - (causal ? 4 * kt : 0), 0) *
+                                       (L.hq / L.hkv) + 2,
+                               (int)(kv_tiles + kt));
+        kv_tiles += nkt;
       }
       if (kv_tiles * L.hkv > 0x7fffffffLL)
         return fail(RA_ERR_UNSUPPORTED, "rank-fused backward: too many key tiles");
     }
     rk.kv_tile_off[d->cp_size] = (int32_t)kv_tiles;
+    // dK/dV: each kv head's key tiles heaviest first where they fit the
+    // order (the causal diagonal's tiles shrink along the block, and a
+    // workgroup holds a CU for its whole query walk); the dQ launch gets its
+    // own copy of the arguments
+    ra::RankKV rkq = rk;
+    rk.tile_ordered = kv_tiles <= ra::kMaxTileOrder;
+    if (rk.tile_ordered) {
+      std::stable_sort(kv_cost.begin(), kv_cost.end(),
+                       [](const std::pair<long long, int>& x, const std::pair<long long, int>& y) {
+                         return x.first > y.first;
+                       });
+      for (size_t u = 0; u < kv_cost.size(); ++u) rk.tile_order[u] = (uint16_t)kv_cost[u].second;
+    }
     const long long q_tiles = rank_q_tiles(L);
     if (q_tiles * L.hq * kMaxQsplit > 0x7fffffffLL)
       return fail(RA_ERR_UNSUPPORTED, "rank-fused backward: too many query tiles");
-    rk.q_tiles = (int32_t)q_tiles;
-    // the dQ tiles walk the blocks as the forward's do: same heaviest-first order
-    if (L.n_seq > 1 && (st = order_packed_tiles(L, d->cp_size, d->rank, 128, false, &rk,
-                                                &rk.q_tiles)) != RA_OK)
+    rkq.q_tiles = (int32_t)q_tiles;
+    // the dQ tiles walk the blocks as the forward's do: same heaviest-first
+    // order over packed segments (a single sequence's tiles already run
+    // heaviest first: last rows first)
+    if (L.n_seq > 1 && (st = order_packed_tiles(L, d->cp_size, d->rank, 128, false, &rkq,
+                                                &rkq.q_tiles)) != RA_OK)
       return st;
     ra_attn_desc sd = L;
     sd.k = d->k_blocks[0];
@@ -1153,7 +1177,7 @@ ra_status ra_rank_backward(const ra_rank_bwd_desc* d, void* stream) {
                              delta, hs);
     if (e != hipSuccess) return hip_fail(e, "delta launch");
     if (a.n_qtiles > 0) {
-      e = ra::launch_rank_bwd_bf16(a, rk, rg, L.dqk, L.dv, hs);
+      e = ra::launch_rank_bwd_bf16(a, rk, rkq, rg, L.dqk, L.dv, hs);
       if (e == hipErrorInvalidValue) return fail(RA_ERR_UNSUPPORTED, "backward variant not built");
       if (e != hipSuccess) return hip_fail(e, "rank backward launch");
     }

@@ -145,7 +145,8 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a, RankKV
   // the XCD's L2 (dealt over the XCDs, every L2 fetched every head's tiles;
   // 32K GQA backward 478 -> 284 TFLOP/s).  The diagonal block comes first.
   // A rank share's grid holds only live tiles: per kv head, the ring steps
-  // in order, each with its owner's live tiles segment by segment.
+  // in order, each with its owner's live tiles segment by segment, taken in
+  // the host's heaviest-first order when it fits the kernel arguments.
   int b = (!RANK && a.n_seq > 1) ? xcd_deal(blockIdx.x, gridDim.x, nsp)
                                  : xcd_remap(blockIdx.x, gridDim.x);
   const int sp = b % nsp;
@@ -156,6 +157,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a, RankKV
     const int per_head = rk.kv_tile_off[rk.cp];
     kvh = b / per_head;
     int r = b - kvh * per_head;
+    if (rk.tile_ordered) r = rk.tile_order[r];  // the host's heaviest-first order
     while (step_o + 1 < rk.cp && r >= rk.kv_tile_off[step_o + 1]) ++step_o;
     r -= rk.kv_tile_off[step_o];
     owner_plan(rk.rank, (rk.rank - step_o + rk.cp) % rk.cp, &own_causal, &own_qp, &own_kp);
@@ -984,8 +986,8 @@ hipError_t launch_attn_bwd_bf16(const AttnArgs& a0, int dqk, int dv, bool causal
   return hipGetLastError();
 }
 
-hipError_t launch_rank_bwd_bf16(const AttnArgs& a0, const RankKV& rk, const RankGrad& rg, int dqk,
-                                int dv, hipStream_t st) {
+hipError_t launch_rank_bwd_bf16(const AttnArgs& a0, const RankKV& rk, const RankKV& rkq,
+                                const RankGrad& rg, int dqk, int dv, hipStream_t st) {
   // the dQ grid is kv heads x rk.q_tiles live 128-row query tiles x group x
   // key shares, the dK/dV grid kv heads x rk.kv_tile_off[rk.cp] live
   // 128-key tiles
@@ -994,7 +996,7 @@ hipError_t launch_rank_bwd_bf16(const AttnArgs& a0, const RankKV& rk, const Rank
   a.k_part = RA_PART_ALL;
   a.qsplit = 1;
   if (a.ksplit < 1 || !a.dq_part) a.ksplit = 1;
-  const long long nq = (long long)a.hkv * rk.q_tiles * a.group * a.ksplit;
+  const long long nq = (long long)a.hkv * rkq.q_tiles * a.group * a.ksplit;
   const long long nk = (long long)a.hkv * rk.kv_tile_off[rk.cp];
   if (nq > 0x7fffffffLL || nk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (dqk == 128 && dv == 128) {
@@ -1003,14 +1005,14 @@ hipError_t launch_rank_bwd_bf16(const AttnArgs& a0, const RankKV& rk, const Rank
                          dim3(NT), 0, st, a, rk, rg);
     if (nq > 0)
       hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 128, false, true>), dim3((unsigned)nq),
-                         dim3(NT), 0, st, a, rk);
+                         dim3(NT), 0, st, a, rkq);
   } else if (dqk == 192 && dv == 128) {
     if (nk > 0)
       hipLaunchKernelGGL((attn_bwd_dkdv_kernel<192, 128, false, false, true>), dim3((unsigned)nk),
                          dim3(NT), 0, st, a, rk, rg);
     if (nq > 0)
       hipLaunchKernelGGL((attn_bwd_dq_kernel<192, 128, false, true>), dim3((unsigned)nq),
-                         dim3(NT), 0, st, a, rk);
+                         dim3(NT), 0, st, a, rkq);
   } else {
     return hipErrorInvalidValue;
   }

@@ -87,7 +87,9 @@ struct RankKV {
   int32_t kv_tile_off[kMaxCp + 1];
   // rank-fused dQ launch: 128-row query tiles of the local rows, segment by
   // segment (the grid per kv head, times the group and the key shares);
-  // over packed segments taken in tile_order as the forward's tiles are
+  // over packed segments taken in tile_order as the forward's tiles are.
+  // The rank-fused dK/dV launch takes its live key tiles (kv_tile_off) in
+  // tile_order if tile_ordered.
   int32_t q_tiles;
   // rank-fused forward over packed segments: fwd_tiles query tiles (256
   // rows on the ping-pong kernel, half tiles if AttnArgs::half_tiles; 128
@@ -188,8 +190,8 @@ hipError_t launch_attn_bwd_bf16(const AttnArgs& a, int dqk, int dv, bool causal,
 // over a.ksplit workgroups, partials reduced in share order).  a describes
 // the rank's local rows (q, dout, lse, delta, dq; parts ALL); rk the
 // owners' K/V blocks.
-hipError_t launch_rank_bwd_bf16(const AttnArgs& a, const RankKV& rk, const RankGrad& rg, int dqk,
-                                int dv, hipStream_t st);
+hipError_t launch_rank_bwd_bf16(const AttnArgs& a, const RankKV& rk_kv, const RankKV& rk_q,
+                                const RankGrad& rg, int dqk, int dv, hipStream_t st);
 
 // Sets the thread-local message ra_last_error() returns and passes st back.
 ra_status set_error(ra_status st, const char* fmt, ...);
