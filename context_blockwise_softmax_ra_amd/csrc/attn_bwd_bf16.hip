@@ -446,7 +446,9 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a, RankKV
 
   // C rows = keys 8*(i/4) + 4g + i%4 of the wave, column = dim 32*nt + l32
   const float scale = a.scale;
-  if (sp == 0) {
+  if (sp == 0 && QS) {
+    // (the query-split form keeps one load-add-store per key row: its
+    // waves' reduction leaves no registers for a batch)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kr = wk_rel + 8 * (i >> 2) + 4 * g + (i & 3);
@@ -458,6 +460,48 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a, RankKV
       for (int nt = 0; nt < G::NQT; ++nt) dkp[32 * nt] += scale * dk[nt][i];
 #pragma unroll
       for (int nt = 0; nt < G::NVT; ++nt) dvp[32 * nt] += dv[nt][i];
+    }
+  } else if (sp == 0) {
+    // Add into the owner's float32 dK, then dV, each as one batch: every
+    // old value is loaded before the first store.  Written as a
+    // load-add-store per key row, the compiler cannot tell the rows'
+    // addresses apart and waits a full memory round trip per row (32 per
+    // wave), which dominated workgroups with few query iterations.  Rows
+    // past the block load the last key's values and store nothing.
+    auto row_of = [&](int i) { return wk_rel + 8 * (i >> 2) + 4 * g + (i & 3); };
+    {
+      float old[16][G::NQT];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t key = k_lo + min(row_of(i), klen - 1);
+        const float* p = dkptr + (key * a.hkv + kvh) * DQK + l32;
+#pragma unroll
+        for (int nt = 0; nt < G::NQT; ++nt) old[i][nt] = p[32 * nt];
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (row_of(i) >= klen) continue;
+        float* p = dkptr + ((k_lo + row_of(i)) * (int64_t)a.hkv + kvh) * DQK + l32;
+#pragma unroll
+        for (int nt = 0; nt < G::NQT; ++nt) p[32 * nt] = old[i][nt] + scale * dk[nt][i];
+      }
+    }
+    {
+      float old[16][G::NVT];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t key = k_lo + min(row_of(i), klen - 1);
+        const float* p = dvptr + (key * a.hkv + kvh) * DV + l32;
+#pragma unroll
+        for (int nt = 0; nt < G::NVT; ++nt) old[i][nt] = p[32 * nt];
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (row_of(i) >= klen) continue;
+        float* p = dvptr + ((k_lo + row_of(i)) * (int64_t)a.hkv + kvh) * DV + l32;
+#pragma unroll
+        for (int nt = 0; nt < G::NVT; ++nt) p[32 * nt] = old[i][nt] + dv[nt][i];
+      }
     }
   } else {
     const int64_t row0 = (int64_t)(sp - 1) * a.part_keys;
