@@ -643,23 +643,26 @@ ra_status ra_rank_forward_workspace(const ra_rank_desc* d, size_t* bytes) {
   return ok();
 }
 
-// Query tiles (bm rows) of a packed rank share: their number, and (up to
-// kMaxTileOrder tiles) the order in which the launch takes them.
-// The work of a tile is estimated by the 64-key tiles it visits over the
-// ring's blocks (the kernel's block walk); heaviest first is the
-// longest-processing-time order, so a launch over many short documents and
-// a few long ones does not end on a long document's tiles.  The tile list
-// is segment by segment, each segment's heaviest (last) tile first.
+// Query tiles (bm rows) of a packed rank share: their number, and the order
+// in which the launch takes them.  The work of a tile is estimated by the
+// 64-key tiles it visits over the ring's blocks (the kernel's block walk);
+// heaviest first is the longest-processing-time order, so a launch over
+// many short documents and a few long ones does not end on a long
+// document's tiles.  The tile list is segment by segment, each segment's
+// heaviest (last) tile first.  Up to kMaxTileOrder tiles the order is by
+// tile (tile_ordered = 1); beyond, up to kMaxTileOrder segments, by segment,
+// each ranked by its heaviest tile (tile_ordered = 2); beyond that the list
+// order stands.
 static ra_status order_packed_tiles(const ra_attn_desc& L, int C, int rank, int bm,
                                      bool half_tiles, ra::RankKV* rk, int32_t* n_tiles) {
-  std::vector<std::pair<long long, int>> cost;  // (estimated work, tile)
+  std::vector<std::pair<long long, int>> cost, seg_cost;  // (estimated work, tile or segment)
   long long n = 0;
   for (int s = 0; s < L.n_seq; ++s) {
     const int len = L.cu_seqlens_q_host[s + 1] - L.cu_seqlens_q_host[s], half = len / 2;
     const int nh = half_tiles ? (half + bm - 1) / bm : 0;
     const int nt = half_tiles ? nh + (len - half + bm - 1) / bm : (len + bm - 1) / bm;
+    long long heaviest = 0;
     for (int i = 0; i < nt; ++i, ++n) {
-      if (n >= ra::kMaxTileOrder) continue;
       const int qt = nt - 1 - i;
       long long q0 = (long long)qt * bm, t_hi = len;
       if (half_tiles) {
@@ -676,18 +679,25 @@ static ra_status order_packed_tiles(const ra_attn_desc& L, int C, int rank, int 
         else kend = last >= half ? len : 0;
         w += (kend + 63) / 64;
       }
-      cost.emplace_back(w, (int)n);
+      if (n < ra::kMaxTileOrder) cost.emplace_back(w, (int)n);
+      heaviest = std::max(heaviest, w);
     }
+    if (s < ra::kMaxTileOrder) seg_cost.emplace_back(heaviest, s);
   }
   if (n * L.hq > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "too many query tiles");
   *n_tiles = (int32_t)n;
-  rk->tile_ordered = n <= ra::kMaxTileOrder;
-  if (rk->tile_ordered) {
-    std::stable_sort(cost.begin(), cost.end(),
-                     [](const std::pair<long long, int>& x, const std::pair<long long, int>& y) {
-                       return x.first > y.first;
-                     });
+  auto by_cost = [](const std::pair<long long, int>& x, const std::pair<long long, int>& y) {
+    return x.first > y.first;
+  };
+  rk->tile_ordered = 0;
+  if (n <= ra::kMaxTileOrder) {
+    rk->tile_ordered = 1;
+    std::stable_sort(cost.begin(), cost.end(), by_cost);
     for (int u = 0; u < (int)n; ++u) rk->tile_order[u] = (uint16_t)cost[u].second;
+  } else if (L.n_seq <= ra::kMaxTileOrder) {
+    rk->tile_ordered = 2;
+    std::stable_sort(seg_cost.begin(), seg_cost.end(), by_cost);
+    for (int u = 0; u < L.n_seq; ++u) rk->tile_order[u] = (uint16_t)seg_cost[u].second;
   }
   return RA_OK;
 }
@@ -1135,7 +1145,7 @@ ra_status ra_rank_backward(const ra_rank_bwd_desc* d, void* stream) {
     // workgroup holds a CU for its whole query walk); the dQ launch gets its
     // own copy of the arguments
     ra::RankKV rkq = rk;
-    rk.tile_ordered = kv_tiles <= ra::kMaxTileOrder;
+    rk.tile_ordered = kv_tiles <= ra::kMaxTileOrder ? 1 : 0;
     if (rk.tile_ordered) {
       std::stable_sort(kv_cost.begin(), kv_cost.end(),
                        [](const std::pair<long long, int>& x, const std::pair<long long, int>& y) {

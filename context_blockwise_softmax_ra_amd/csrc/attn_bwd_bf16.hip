@@ -92,16 +92,23 @@ struct GeoKV {
 // Tile r of the live 128-key (BY_KEYS) or 128-row tiles of a block in the
 // rank-fused grids: a segment contributes ceil(length / 128) tiles along
 // that axis if some row of its query part sees some key of its key part.
-template <bool BY_KEYS>
+// seg_at(i) is the segment the grid takes i-th.  (A functor that reads the
+// kernel argument directly: a pointer into a by-value kernel argument makes
+// the compiler copy the whole argument to scratch memory.)
+template <bool BY_KEYS, class SegAt>
 __device__ __forceinline__ bool locate_tile(const int32_t* cu_q, const int32_t* cu_k, int n_seq,
-                                            int qp, int kp, int r, int* seg, int* idx, int* cnt) {
+                                            int qp, int kp, int r, int* seg, int* idx, int* cnt,
+                                            SegAt seg_at) {
   auto count = [&](int s) {
+    s = seg_at(s);
     int ql, qh, kl, kh;
     part_range(cu_q[s], cu_q[s + 1], qp, &ql, &qh);
     part_range(cu_k[s], cu_k[s + 1], kp, &kl, &kh);
     return (qh > ql && kh > kl) ? ((BY_KEYS ? kh - kl : qh - ql) + 127) / 128 : 0;
   };
-  return locate_in_segments(n_seq, r, count, seg, idx, cnt);
+  if (!locate_in_segments(n_seq, r, count, seg, idx, cnt)) return false;
+  *seg = seg_at(*seg);
+  return true;
 }
 
 // QS ("query split"): a workgroup covers 32 keys and its 4 waves split the
@@ -157,7 +164,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a, RankKV
     const int per_head = rk.kv_tile_off[rk.cp];
     kvh = b / per_head;
     int r = b - kvh * per_head;
-    if (rk.tile_ordered) r = rk.tile_order[r];  // the host's heaviest-first order
+    if (rk.tile_ordered == 1) r = rk.tile_order[r];  // the host's heaviest-first order
     while (step_o + 1 < rk.cp && r >= rk.kv_tile_off[step_o + 1]) ++step_o;
     r -= rk.kv_tile_off[step_o];
     owner_plan(rk.rank, (rk.rank - step_o + rk.cp) % rk.cp, &own_causal, &own_qp, &own_kp);
@@ -166,7 +173,9 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(AttnArgs a, RankKV
       kt = r;
     } else {
       int cnt;
-      if (!locate_tile<true>(a.cu_q, a.cu_k, a.n_seq, own_qp, own_kp, r, &seg, &kt, &cnt)) return;
+      if (!locate_tile<true>(a.cu_q, a.cu_k, a.n_seq, own_qp, own_kp, r, &seg, &kt, &cnt,
+                             [](int i) { return i; }))
+        return;
     }
   } else {
     kt = b % a.n_ktiles;
@@ -631,9 +640,10 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a, RankKV r
       seg = 0;
       idx = r;
       cnt = a.n_qtiles;
-    } else if (!locate_tile<false>(a.cu_q, a.cu_k, a.n_seq, RA_PART_ALL, RA_PART_ALL,
-                                   rk.tile_ordered ? (int)rk.tile_order[r] : r, &seg, &idx,
-                                   &cnt)) {
+    } else if (!locate_tile<false>(
+                   a.cu_q, a.cu_k, a.n_seq, RA_PART_ALL, RA_PART_ALL,
+                   rk.tile_ordered == 1 ? (int)rk.tile_order[r] : r, &seg, &idx, &cnt,
+                   [&](int i) { return rk.tile_ordered == 2 ? (int)rk.tile_order[i] : i; })) {
       return;
     }
     qt = cnt - 1 - idx;

@@ -86,16 +86,22 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
   int kvh, seg, kv_part = 0, qt;  // kv_part: part of a KV-split rank share
   if (MODE == 2 && a.n_seq > 1) {
     // packed documents: only live tiles, the kv heads of one tile together,
-    // tiles in the host's heaviest-first order (or segment by segment, each
-    // segment's heaviest tile first), parts slowest
+    // segment by segment with each segment's heaviest tile first, taken in
+    // the host's heaviest-first order of tiles (tile_ordered 1) or of
+    // segments (2); parts slowest
     kvh = b % a.hkv;
     b /= a.hkv;
     const int u = b % rk.fwd_tiles;
     kv_part = b / rk.fwd_tiles;
-    const int j = rk.tile_ordered ? (int)rk.tile_order[u] : u;
-    auto count = [&](int s) { return (a.cu_q[s + 1] - a.cu_q[s] + BM - 1) / BM; };
+    const int j = rk.tile_ordered == 1 ? (int)rk.tile_order[u] : u;
+    auto seg_at = [&](int s) { return rk.tile_ordered == 2 ? (int)rk.tile_order[s] : s; };
+    auto count = [&](int s) {
+      s = seg_at(s);
+      return (a.cu_q[s + 1] - a.cu_q[s] + BM - 1) / BM;
+    };
     int idx, cnt;
     if (!locate_in_segments(a.n_seq, j, count, &seg, &idx, &cnt)) return;
+    seg = seg_at(seg);
     qt = cnt - 1 - idx;
   } else {
     const int qt_rev = b % a.n_qtiles;

@@ -99,18 +99,22 @@ __global__ __launch_bounds__(PT, 1) void attn_fwd_pp_kernel(AttnArgs a, RankKV r
   int kvh, seg, qt;
   if (MODE == 2 && a.n_seq > 1) {
     // packed documents: only live tiles, the kv heads of one tile
-    // together, tiles in the host's heaviest-first order (or segment by
-    // segment, each segment's heaviest tile first)
+    // together, segment by segment with each segment's heaviest tile first,
+    // taken in the host's heaviest-first order of tiles (tile_ordered 1) or
+    // of segments (2)
     kvh = b % a.hkv;
     const int u = b / a.hkv;
-    const int j = rk.tile_ordered ? (int)rk.tile_order[u] : u;
+    const int j = rk.tile_ordered == 1 ? (int)rk.tile_order[u] : u;
+    auto seg_at = [&](int s) { return rk.tile_ordered == 2 ? (int)rk.tile_order[s] : s; };
     auto count = [&](int s) {
+      s = seg_at(s);
       const int len = a.cu_q[s + 1] - a.cu_q[s], half = len >> 1;
       return a.half_tiles ? (half + PBM - 1) / PBM + (len - half + PBM - 1) / PBM
                           : (len + PBM - 1) / PBM;
     };
     int idx, cnt;
     if (!locate_in_segments(a.n_seq, j, count, &seg, &idx, &cnt)) return;
+    seg = seg_at(seg);
     qt = cnt - 1 - idx;
   } else {
     const int qt_rev = b % n_qtiles;

@@ -94,9 +94,11 @@ struct RankKV {
   // rank-fused forward over packed segments: fwd_tiles query tiles (256
   // rows on the ping-pong kernel, half tiles if AttnArgs::half_tiles; 128
   // on the 4-wave kernel) of all segments, listed segment by segment with
-  // each segment's heaviest tile first; if tile_ordered, workgroup unit u
+  // each segment's heaviest tile first.  tile_ordered 1: workgroup unit u
   // (all kv heads of one tile) takes tile tile_order[u] of that list (the
-  // host's heaviest-first order), else tile u
+  // host's heaviest-first order); 2: the list takes the segments in the
+  // order tile_order[0], tile_order[1], ... (heaviest first, for lists of
+  // more tiles than the order holds); 0: unit u takes tile u
   int32_t fwd_tiles;
   int32_t tile_ordered;
   uint16_t tile_order[kMaxTileOrder];

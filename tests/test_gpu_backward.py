@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import check_out, log, make_problem, metrics, sample_rows, to_np
+from gpu_util import check_lse, check_out, log, make_problem, metrics, sample_rows, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -278,6 +278,64 @@ def test_backward_many_documents_parity(mode, monkeypatch):
     w.doc_lengths = [4 * (1 + i % 10) for i in range(160)] + [576]
     assert sum(w.doc_lengths) == 4096 and len(w.doc_lengths) > 128
     _full_bwd_parity(w, dout_scale=0.25)
+
+
+def _per_document_reference(q64, k64, v64, do64, cu):
+    """The oracle's forward and gradients, one document at a time (documents
+    are independent, so this equals the whole-stream call)."""
+    lay = oracle.ref.Layout(cu)
+    ro = np.zeros(q64.shape[:2] + (v64.shape[2],))
+    rl = np.zeros((q64.shape[1], q64.shape[0]))
+    rq, rk, rv = np.zeros_like(q64), np.zeros_like(k64), np.zeros_like(v64)
+    for d in range(len(cu) - 1):
+        s = slice(int(cu[d]), int(cu[d + 1]))
+        args = (lay.pos[s], lay.doc[s], lay.pos[s], lay.doc[s])
+        ro[s], rl[:, s] = oracle.attention(q64[s], k64[s], v64[s], *args)
+        rq[s], rk[s], rv[s] = oracle.attention_bwd(q64[s], k64[s], v64[s], do64[s], *args)
+    return ro, rl, rq, rk, rv
+
+
+# Packed streams whose tile lists take each ordering of the rank-fused
+# grids: heaviest-first by tile (up to 512 tiles), by segment (more tiles,
+# at most 512 segments) and the plain list order (more segments).
+TILE_ORDER_CASES = {
+    # ping-pong forward: 602 half tiles of 300 segments (by segment); 4-wave
+    # forward and dQ: 306 tiles (by tile)
+    "fwd_by_segment": (2, [8] * 299 + [1704], 16),
+    # 600 segments: every launch in list order
+    "list_order": (2, [4] * 599 + [1700], 16),
+    # one rank (cp 1), 200 documents of 384: dQ and the 4-wave forward 600
+    # tiles (by segment), ping-pong forward 400 (by tile)
+    "dq_by_segment": (1, [384] * 200, 2),
+}
+
+
+@pytest.mark.parametrize("kernel", ["4w", "pp"])
+@pytest.mark.parametrize("case", list(TILE_ORDER_CASES))
+def test_packed_tile_orders_parity(case, kernel, monkeypatch):
+    """Every output of every rank (forward out/lse, dQ, dK, dV) against the
+    oracle, per document, for each ordering of the packed grids."""
+    cp, docs, heads = TILE_ORDER_CASES[case]
+    _set_splits(monkeypatch, "auto")
+    monkeypatch.setenv("RA_FWD_KERNEL", kernel)
+    w = synth.reduced("varlen_128k", sum(docs), cp, hq=heads, hkv=heads)
+    w.doc_lengths = list(docs)
+    log(f"{case} kernel={kernel}: {len(docs)} documents, S={w.seqlen} C={cp} heads={heads}")
+    prob, (q, k, v, do) = make_problem(w, with_dout=True, dout_scale=0.25)
+    q64, k64, v64, do64 = to_np(q), to_np(k), to_np(v), to_np(do)
+    ro, rl, rq, rk, rv = _per_document_reference(q64, k64, v64, do64, w.cu_global())
+    outs, lses, dqs, dks, dvs = _run_ranks(prob)
+    for r in range(cp):
+        rows = prob.rows(r)
+        check_out(to_np(outs[r]), ro[rows], "bf16", f"rank{r} out")
+        check_lse(to_np(lses[r]), rl[:, rows], f"rank{r} lse")
+    gq, gk, gv = np.zeros_like(rq), np.zeros_like(rk), np.zeros_like(rv)
+    for r in range(cp):
+        rows = prob.rows(r)
+        gq[rows], gk[rows], gv[rows] = to_np(dqs[r]), to_np(dks[r]), to_np(dvs[r])
+    check_out(gq, rq, "bf16", "dQ")
+    check_out(gk, rk, "bf16", "dK")
+    check_out(gv, rv, "bf16", "dV")
 
 
 @pytest.mark.parametrize("mode", ["auto", "fused_ksplit4", "step_auto", "qsplit1",
