@@ -605,6 +605,88 @@ static int fwd_kv_split(const ra_rank_desc* d, const Checked& c) {
   return 1;
 }
 
+// 64-key tiles visited over the ring's blocks by query tile qt (bm rows) of
+// a local segment of len rows (nh first-chunk tiles if half tiles): the
+// owner's own block up to the tile's last row, an earlier owner's first
+// key half, a later owner's whole block if the tile holds second-half rows.
+static long long tile_walk(int len, int qt, int nh, int bm, bool half_tiles, int C, int rank) {
+  const int half = len / 2;
+  long long q0 = (long long)qt * bm, t_hi = len;
+  if (half_tiles) {
+    if (qt < nh) t_hi = half;
+    else q0 = half + (long long)(qt - nh) * bm;
+  }
+  const long long last = std::min(q0 + bm, t_hi) - 1;
+  long long w = 0;
+  for (int o = 0; o < C; ++o) {
+    const int owner = (rank - o + C) % C;
+    long long kend;
+    if (o == 0) kend = std::min<long long>(len, last + 1);
+    else if (owner < rank) kend = half;
+    else kend = last >= half ? len : 0;
+    w += (kend + 63) / 64;
+  }
+  return w;
+}
+
+// Per-tile parts for a single sequence split for its size.  A uniform split
+// gives every query tile the same number of parts, but the tiles' walks
+// differ up to ~60x (second-half rows of early ranks see every later
+// owner's whole block), and the launch is one round of workgroups: its
+// length is the heaviest tile's part.  With per-tile parts the same number
+// of workgroups (split x tiles) is dealt by the tiles' walks (greedy: the
+// next part goes to the tile with the longest part), at most `slots` parts
+// per tile; parts are taken heaviest first.  Returns the number of partial
+// slots (0: the share keeps the uniform split).  RA_FWD_VAR_SPLIT=0 in the
+// environment keeps it uniform.
+constexpr int kVarSplitSlots = 6;
+static int fwd_var_slots(const ra_rank_desc* d, int split) {
+  const ra_attn_desc& L = d->local;
+  if (split <= 1 || split > 8 || L.n_seq != 1) return 0;
+  const char* e = std::getenv("RA_FWD_VAR_SPLIT");
+  if (e && !std::strcmp(e, "0")) return 0;
+  const long long tiles =
+      (L.cu_seqlens_q_host[1] - L.cu_seqlens_q_host[0] + ra::kFwdBlockM - 1) / ra::kFwdBlockM;
+  if (tiles <= 0 || tiles * split > ra::kMaxTileOrder) return 0;
+  // the size rule's small shares (or a forced split)
+  const char* f = std::getenv("RA_FWD_KV_SPLIT");
+  if (!(f && *f) && tiles * L.hq >= 256) return 0;
+  return std::max(split, kVarSplitSlots);
+}
+
+// The per-tile parts of a single-sequence share into rk: tile_order[u] is
+// unit u's (query tile << 6 | part << 3 | parts - 1), heaviest part first,
+// fwd_tiles the number of units per head.
+static void plan_var_split(const ra_rank_desc* d, int split, int slots, ra::RankKV* rk) {
+  const ra_attn_desc& L = d->local;
+  const int len = L.cu_seqlens_q_host[1] - L.cu_seqlens_q_host[0];
+  const int nt = (len + ra::kFwdBlockM - 1) / ra::kFwdBlockM;
+  std::vector<long long> w(nt);
+  for (int t = 0; t < nt; ++t)
+    w[t] = tile_walk(len, t, 0, ra::kFwdBlockM, false, d->cp_size, d->rank);
+  std::vector<int> parts(nt, 1);
+  for (long long n = nt; n < (long long)split * nt; ++n) {
+    int best = -1;
+    for (int t = 0; t < nt; ++t)  // longest part (ceil) among tiles that can split further
+      if (parts[t] < slots && parts[t] < w[t] &&
+          (best < 0 || (w[t] + parts[t] - 1) / parts[t] > (w[best] + parts[best] - 1) / parts[best]))
+        best = t;
+    if (best < 0) break;
+    ++parts[best];
+  }
+  std::vector<std::pair<long long, int>> units;  // (part length, entry)
+  for (int t = 0; t < nt; ++t)
+    for (int q = 0; q < parts[t]; ++q)
+      units.emplace_back((w[t] - q + parts[t] - 1) / parts[t], (t << 6) | (q << 3) | (parts[t] - 1));
+  std::stable_sort(units.begin(), units.end(),
+                   [](const std::pair<long long, int>& x, const std::pair<long long, int>& y) {
+                     return x.first > y.first;
+                   });
+  for (size_t u = 0; u < units.size(); ++u) rk->tile_order[u] = (uint16_t)units[u].second;
+  rk->fwd_tiles = (int32_t)units.size();
+  rk->var_split = 1;
+}
+
 // Half tiles (ping-pong kernel, fused rank share of packed documents):
 // tile each zig-zag chunk of a document on its own.  A 256-row tile that
 // straddles a document's two chunks runs the later owners' blocks, which
@@ -634,7 +716,8 @@ ra_status ra_rank_forward_workspace(const ra_rank_desc* d, size_t* bytes) {
     // one launch writing the output directly, or with a KV split the
     // float32 partials of every part
     const int split = fwd_kv_split(d, c);
-    *bytes = split > 1 ? (size_t)split * (out_b + lse_b) : 0;
+    const int slots = fwd_var_slots(d, split);
+    *bytes = split > 1 ? (size_t)(slots ? slots : split) * (out_b + lse_b) : 0;
     return ok();
   }
   if (d->out_dtype != RA_FP32) b += out_b;                   // fp32 accumulator
@@ -663,22 +746,7 @@ static ra_status order_packed_tiles(const ra_attn_desc& L, int C, int rank, int 
     const int nt = half_tiles ? nh + (len - half + bm - 1) / bm : (len + bm - 1) / bm;
     long long heaviest = 0;
     for (int i = 0; i < nt; ++i, ++n) {
-      const int qt = nt - 1 - i;
-      long long q0 = (long long)qt * bm, t_hi = len;
-      if (half_tiles) {
-        if (qt < nh) t_hi = half;
-        else q0 = half + (long long)(qt - nh) * bm;
-      }
-      const long long last = std::min(q0 + bm, t_hi) - 1;
-      long long w = 0;
-      for (int o = 0; o < C; ++o) {
-        const int owner = (rank - o + C) % C;
-        long long kend;
-        if (o == 0) kend = std::min<long long>(len, last + 1);
-        else if (owner < rank) kend = half;
-        else kend = last >= half ? len : 0;
-        w += (kend + 63) / 64;
-      }
+      const long long w = tile_walk(len, nt - 1 - i, nh, bm, half_tiles, C, rank);
       if (n < ra::kMaxTileOrder) cost.emplace_back(w, (int)n);
       heaviest = std::max(heaviest, w);
     }
@@ -745,7 +813,12 @@ ra_status ra_rank_forward(const ra_rank_desc* d, void* stream) {
     ra::AttnArgs a = make_args(&sd, cs);
     a.out = static_cast<float*>(d->out);
     a.lse = d->lse;
-    const int split = fwd_kv_split(d, c);
+    int split = fwd_kv_split(d, c);
+    const int slots = fwd_var_slots(d, split);
+    if (slots) {
+      plan_var_split(d, split, slots, &rk);
+      split = slots;  // partial slots; unused ones get lse = -inf from the tile's part 0
+    }
     rk.split = split;
     const size_t out_b = align256((size_t)c.total_q * L.hq * L.dv * sizeof(float));
     const size_t lse_b = align256((size_t)c.total_q * L.hq * sizeof(float));

@@ -79,12 +79,24 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
   // rank share of packed documents (units of very unequal size, one
   // document's after another in logical order): deal query tiles over the
   // XCDs; otherwise contiguous ranges per XCD
-  const bool causal_only = MODE == 1 || MODE == 3 || (MODE == 2 && (rk.cp == 1 || a.n_seq > 1));
+  const bool causal_only =
+      MODE == 1 || MODE == 3 || (MODE == 2 && (rk.cp == 1 || a.n_seq > 1 || rk.var_split));
   int b = causal_only ? xcd_deal(blockIdx.x, nb, group) : xcd_remap(blockIdx.x, nb);
   const int hg = b % group;
   b /= group;
-  int kvh, seg, kv_part = 0, qt;  // kv_part: part of a KV-split rank share
-  if (MODE == 2 && a.n_seq > 1) {
+  // kv_part of kv_split: part of a KV-split rank share; with a KV split this
+  // workgroup takes every kv_split-th key tile of the share's tile
+  // sequence, starting at tile kv_part
+  int kvh, seg, kv_part = 0, qt, kv_split = MODE == 2 ? max(rk.split, 1) : 1;
+  if (MODE == 2 && rk.var_split) {
+    // per-tile parts, heaviest part first, the kv heads of one unit together
+    kvh = b % a.hkv;
+    const int e = rk.tile_order[b / a.hkv];
+    seg = 0;
+    qt = e >> 6;
+    kv_part = (e >> 3) & 7;
+    kv_split = (e & 7) + 1;
+  } else if (MODE == 2 && a.n_seq > 1) {
     // packed documents: only live tiles, the kv heads of one tile together,
     // segment by segment with each segment's heaviest tile first, taken in
     // the host's heaviest-first order of tiles (tile_ordered 1) or of
@@ -149,10 +161,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
   const int my_row = wq0 + l32;
   const int my_row_rel = my_row - q_lo;
   const int64_t ks_bytes = a.k_stride * 2, vs_bytes = a.v_stride * 2;
-  // a rank share's blocks (ring steps), or the one block; with a KV split
-  // this workgroup takes every split-th key tile of the share's tile
-  // sequence, starting at tile kv_part
-  const int kv_split = MODE == 2 ? max(rk.split, 1) : 1;
+  // a rank share's blocks (ring steps), or the one block
   const int nblocks = MODE == 2 ? rk.cp : 1;
 
   // block bi of this workgroup, with the number of key tiles it visits
@@ -405,6 +414,10 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(AttnArgs a, RankKV
   float* const out_base = a.out + (MODE == 2 ? kv_part * rk.part_out_stride : 0);
   float* lrow = a.lse + (MODE == 2 ? kv_part * rk.part_lse_stride : 0) + (int64_t)h * a.total_q +
                 my_row;
+  if (MODE == 2 && rk.var_split && kv_part == 0 && g == 0) {
+    // partial slots past this tile's parts hold nothing: the combine skips them
+    for (int p = kv_split; p < rk.split; ++p) lrow[p * rk.part_lse_stride] = -INFINITY;
+  }
   if (OUT_BF16) {
     // final output straight to bf16 (round to nearest even)
     unsigned short* orow = reinterpret_cast<unsigned short*>(out_base) + ((int64_t)my_row * a.hq + h) * DV;
@@ -466,7 +479,9 @@ hipError_t launch_t(const AttnArgs& a, const RankKV* rk, bool causal, bool merge
   if (rk && split > 1 && out_bf16) return hipErrorInvalidValue;  // parts are float32
   // a packed rank share lists live tiles only (rk->fwd_tiles over all
   // segments)
-  const long long nblk = (rk && a.n_seq > 1)
+  const long long nblk = (rk && rk->var_split)
+                             ? (long long)rk->fwd_tiles * a.hkv * a.group
+                         : (rk && a.n_seq > 1)
                              ? (long long)rk->fwd_tiles * a.hkv * a.group * split
                              : (long long)a.n_seq * a.hkv * a.n_qtiles * a.group * split;
   if (nblk <= 0) return hipSuccess;

@@ -279,7 +279,8 @@ __global__ __launch_bounds__(NT) void split_combine_kernel(
     if (m != -INFINITY) {
       for (int p = 0; p < split; ++p) {
         const float lp = part_lse[p * pl + li];
-        const float w = lp == -INFINITY ? 0.f : __expf(lp - m);
+        if (lp == -INFINITY) continue;  // a part with no key of the row (its out may be unset)
+        const float w = __expf(lp - m);
         const float4 o = reinterpret_cast<const float4*>(part_out + p * po)[i];
         acc.x += w * o.x;
         acc.y += w * o.y;
@@ -307,7 +308,8 @@ __global__ __launch_bounds__(NT) void split_combine_kernel(
   }
 }
 
-// The same for S parts and rows of DV4 float4 (a power of two): each
+// The same for S parts (2, 4, 6 or 8) and rows of DV4 float4 (a power of
+// two): each
 // thread reads its row's S lse values once, and the row index comes from a
 // shift and one 32-bit division (the generic kernel above divides in 64
 // bits twice per float4).
@@ -335,7 +337,8 @@ __global__ __launch_bounds__(NT) void split_combine_fixed_kernel(
   if (m != -INFINITY) {
 #pragma unroll
     for (int p = 0; p < S; ++p) {
-      const float w = lp[p] == -INFINITY ? 0.f : __expf(lp[p] - m);
+      if (lp[p] == -INFINITY) continue;  // a part with no key of the row (its out may be unset)
+      const float w = __expf(lp[p] - m);
       const float4 o = reinterpret_cast<const float4*>(part_out + p * po)[i];
       acc.x += w * o.x;
       acc.y += w * o.y;
@@ -428,9 +431,11 @@ hipError_t launch_split_combine(const float* part_out, const float* part_lse, in
   if (n < ((int64_t)1 << 31)) {
     RA_COMBINE_FIXED(2, 32)
     RA_COMBINE_FIXED(4, 32)
+    RA_COMBINE_FIXED(6, 32)
     RA_COMBINE_FIXED(8, 32)
     RA_COMBINE_FIXED(2, 16)
     RA_COMBINE_FIXED(4, 16)
+    RA_COMBINE_FIXED(6, 16)
     RA_COMBINE_FIXED(8, 16)
   }
 #undef RA_COMBINE_FIXED

@@ -101,6 +101,11 @@ struct RankKV {
   // more tiles than the order holds); 0: unit u takes tile u
   int32_t fwd_tiles;
   int32_t tile_ordered;
+  // KV split with per-tile parts (4-wave kernel, single sequence): unit u
+  // of fwd_tiles per head is tile_order[u] = query tile << 6 | part << 3 |
+  // parts - 1; split is then the number of partial slots, and part 0 of a
+  // tile sets lse = -inf in the slots past its tile's parts
+  int32_t var_split;
   uint16_t tile_order[kMaxTileOrder];
 };
 

@@ -231,12 +231,18 @@ def test_rank_forward_workspace_sizes():
     ("mla_256k", None, 2),     # 4-wave kernel, 1024 workgroups, rows see ~131K keys
     ("gqa_32k", "4w", 0),      # 1024 workgroups but ~16K keys per row: not split
     ("gqa_32k", None, 0),      # ping-pong kernel: never split
-    ("mha_8k", None, 4),       # 128 workgroups: split to fill the CUs
+    ("mha_8k", None, 6),       # 128 workgroups: split to fill the CUs, per-tile parts (6 slots)
+    ("mha_8k", "uniform", 4),  # the same with a uniform split: 4 parts
 ])
 def test_fused_forward_kv_split_choice(name, kernel, parts, monkeypatch):
     """Workspace of a fused rank share = the float32 (out, lse) partials of
-    its KV split parts (none when it is not split)."""
+    its KV split parts, or of the partial slots of per-tile parts (none when
+    it is not split)."""
     monkeypatch.delenv("RA_FWD_KV_SPLIT", raising=False)
+    monkeypatch.delenv("RA_FWD_VAR_SPLIT", raising=False)
+    if kernel == "uniform":
+        monkeypatch.setenv("RA_FWD_VAR_SPLIT", "0")
+        kernel = None
     if kernel is None:
         monkeypatch.delenv("RA_FWD_KERNEL", raising=False)
     else:

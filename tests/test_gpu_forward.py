@@ -403,14 +403,18 @@ def _full_parity(w, fuse_modes=(0, 1, 2), determinism=False):
     return prob
 
 
+@pytest.mark.parametrize("var", ["0", "1"], ids=["uniform", "per_tile"])
 @pytest.mark.parametrize("split", ["1", "2", "3", "4", "8", "16"])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
-def test_fused_rank_share_kv_split(split, out_dtype, monkeypatch):
+def test_fused_rank_share_kv_split(split, out_dtype, var, monkeypatch):
     """A fused rank share whose key tiles are dealt over `split` parts (each
     a float32 partial), combined by lse weight (2, 4 and 8 parts by the
     fixed-shape combine, 3 and 16 by the generic one); with 16 parts some
-    workgroups of the first-half rows get no tile at all."""
+    workgroups of the first-half rows get no tile at all.  Per tile: the
+    same number of workgroups dealt over the tiles by their walks (6 or 8
+    partial slots, unused slots marked empty; 16 parts stay uniform)."""
     monkeypatch.setenv("RA_FWD_KV_SPLIT", split)
+    monkeypatch.setenv("RA_FWD_VAR_SPLIT", var)
     w = synth.reduced("gqa_32k", 4096, 8)
     prob, (q, k, v, _) = make_problem(w)
     ro, rl = oracle.full_attention(to_np(q), to_np(k), to_np(v), w.cu_global())
