@@ -204,11 +204,15 @@ ra_status ra_cast_f32_bf16(const float* src, void* dst, int64_t n, void* stream)
  * in part order (deterministic).  The split is taken when the share has
  * fewer than 256 workgroups (128 rows x one query head; up to 8 parts), and
  * in 2 parts when it has 256-2047 workgroups whose rows see on average 64K
- * keys or more (long shares such as 256K MLA).  The workspace is then
- * parts x (out + lse), otherwise 0; since the rule depends on the shapes,
- * callers must always ask ra_rank_forward_workspace for the size (it is the
- * same for every rank of a ring).  The environment variable
- * RA_FWD_KV_SPLIT=<n> forces n parts (1 = none, at most 16).
+ * keys or more (long shares such as 256K MLA).  A single sequence split
+ * for its size deals the same number of workgroups (parts x query tiles)
+ * over the query tiles by the length of their walks, at most 6 parts per
+ * tile (or the split count, if larger), into 6 partial slots.  The
+ * workspace is then slots x (out + lse), otherwise 0; since the rule
+ * depends on the shapes, callers must always ask ra_rank_forward_workspace
+ * for the size (it is the same for every rank of a ring).  The environment
+ * variable RA_FWD_KV_SPLIT=<n> forces n parts (1 = none, at most 16), and
+ * RA_FWD_VAR_SPLIT=0 keeps the parts uniform over the tiles.
  * fp32 falls back to fuse_merge = 1.
  * events (optional): host array of 2*cp_size hipEvent_t, recorded on the
  * stream right before / after step s's attention launch (with
