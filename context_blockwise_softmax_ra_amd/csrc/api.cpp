@@ -654,37 +654,49 @@ static int fwd_var_slots(const ra_rank_desc* d, int split) {
   return std::max(split, kVarSplitSlots);
 }
 
-// The per-tile parts of a single-sequence share into rk: tile_order[u] is
-// unit u's (query tile << 6 | part << 3 | parts - 1), heaviest part first,
-// fwd_tiles the number of units per head.
-static void plan_var_split(const ra_rank_desc* d, int split, int slots, ra::RankKV* rk) {
-  const ra_attn_desc& L = d->local;
-  const int len = L.cu_seqlens_q_host[1] - L.cu_seqlens_q_host[0];
-  const int nt = (len + ra::kFwdBlockM - 1) / ra::kFwdBlockM;
-  std::vector<long long> w(nt);
-  for (int t = 0; t < nt; ++t)
-    w[t] = tile_walk(len, t, 0, ra::kFwdBlockM, false, d->cp_size, d->rank);
+// Deals `total` workgroups over tiles of walk lengths w (at least one per
+// tile, at most `cap`, never more than a tile's walk): each next part goes
+// to the tile whose parts are longest.  Writes the units, heaviest part
+// first, into rk->tile_order as (tile << 6 | part << 3 | parts - 1), sets
+// rk->var_split and returns the number of units; parts[t] (if given)
+// receives each tile's part count.
+static int plan_tile_parts(const std::vector<long long>& w, long long total, int cap,
+                           ra::RankKV* rk, uint8_t* parts_out) {
+  const int nt = (int)w.size();
   std::vector<int> parts(nt, 1);
-  for (long long n = nt; n < (long long)split * nt; ++n) {
+  for (long long n = nt; n < total; ++n) {
     int best = -1;
-    for (int t = 0; t < nt; ++t)  // longest part (ceil) among tiles that can split further
-      if (parts[t] < slots && parts[t] < w[t] &&
+    for (int t = 0; t < nt; ++t)
+      if (parts[t] < cap && parts[t] < w[t] &&
           (best < 0 || (w[t] + parts[t] - 1) / parts[t] > (w[best] + parts[best] - 1) / parts[best]))
         best = t;
     if (best < 0) break;
     ++parts[best];
   }
   std::vector<std::pair<long long, int>> units;  // (part length, entry)
-  for (int t = 0; t < nt; ++t)
+  for (int t = 0; t < nt; ++t) {
+    if (parts_out) parts_out[t] = (uint8_t)parts[t];
     for (int q = 0; q < parts[t]; ++q)
       units.emplace_back((w[t] - q + parts[t] - 1) / parts[t], (t << 6) | (q << 3) | (parts[t] - 1));
+  }
   std::stable_sort(units.begin(), units.end(),
                    [](const std::pair<long long, int>& x, const std::pair<long long, int>& y) {
                      return x.first > y.first;
                    });
   for (size_t u = 0; u < units.size(); ++u) rk->tile_order[u] = (uint16_t)units[u].second;
-  rk->fwd_tiles = (int32_t)units.size();
   rk->var_split = 1;
+  return (int)units.size();
+}
+
+// Walk lengths of a single sequence's 128-row query tiles in a rank share
+// (the 4-wave forward's and the dQ kernel's tile height).
+static_assert(ra::kFwdBlockM == 128, "128-row query tiles");
+static std::vector<long long> single_walks(const ra_attn_desc& L, int C, int rank) {
+  const int len = L.cu_seqlens_q_host[1] - L.cu_seqlens_q_host[0];
+  const int nt = (len + 127) / 128;
+  std::vector<long long> w(nt);
+  for (int t = 0; t < nt; ++t) w[t] = tile_walk(len, t, 0, 128, false, C, rank);
+  return w;
 }
 
 // Half tiles (ping-pong kernel, fused rank share of packed documents):
@@ -816,7 +828,8 @@ ra_status ra_rank_forward(const ra_rank_desc* d, void* stream) {
     int split = fwd_kv_split(d, c);
     const int slots = fwd_var_slots(d, split);
     if (slots) {
-      plan_var_split(d, split, slots, &rk);
+      const std::vector<long long> w = single_walks(L, d->cp_size, d->rank);
+      rk.fwd_tiles = plan_tile_parts(w, (long long)split * (long long)w.size(), slots, &rk, nullptr);
       split = slots;  // partial slots; unused ones get lse = -inf from the tile's part 0
     }
     rk.split = split;
@@ -1104,8 +1117,23 @@ static int bwd_rank_ksplit(const ra_attn_desc& L, const Checked& c) {
   return n;
 }
 
+// Per-tile key shares of a single sequence's rank-fused dQ launch: as the
+// forward's per-tile parts, the ksplit x tiles workgroups are dealt over
+// the query tiles by the length of their walks (at most 6 shares per
+// tile, or ksplit if larger), since the tiles' walks differ up to ~60x.
+// Returns the number of share slots (0: uniform shares).
+// RA_BWD_VAR_SPLIT=0 in the environment keeps the shares uniform.
+static int bwd_var_slots(const ra_attn_desc& L, int ksplit) {
+  if (ksplit <= 1 || L.n_seq != 1) return 0;
+  const char* e = std::getenv("RA_BWD_VAR_SPLIT");
+  if (e && !std::strcmp(e, "0")) return 0;
+  if (rank_q_tiles(L) * ksplit > ra::kMaxTileOrder) return 0;
+  return std::max(ksplit, 6);
+}
+
 // Workspace: delta [hq, total_q], then
-//  - rank-fused: the dQ partials of key shares 1 .. ksplit-1;
+//  - rank-fused: the dQ partials of key shares 1 .. ksplit-1 (of share
+//    slots 1 .. slots-1 with per-tile shares);
 //  - per step: the dK/dV partials of query shares 1 .. qsplit-1 (and dQ
 //    partials) of the step kind that splits most.  Every kind a rank of the
 //    ring can meet is counted (the diagonal block, an earlier and a later
@@ -1118,7 +1146,9 @@ ra_status ra_rank_backward_workspace(const ra_rank_bwd_desc* d, size_t* bytes) {
   const size_t delta_b = align256((size_t)c.total_q * d->local.hq * sizeof(float));
   if (bwd_rank_fused()) {
     const size_t part = align256((size_t)c.total_q * d->local.hq * d->local.dqk * sizeof(float));
-    *bytes = delta_b + (size_t)(bwd_rank_ksplit(d->local, c) - 1) * part;
+    const int ksplit = bwd_rank_ksplit(d->local, c);
+    const int slots = bwd_var_slots(d->local, ksplit);
+    *bytes = delta_b + (size_t)((slots ? slots : ksplit) - 1) * part;
     return ok();
   }
   size_t parts = 0;
@@ -1251,8 +1281,16 @@ ra_status ra_rank_backward(const ra_rank_bwd_desc* d, void* stream) {
     a.delta = delta;
     a.dq = d->dq;
     const int ksplit = bwd_rank_ksplit(L, c);
-    a.ksplit = ksplit;
-    a.dq_part = ksplit > 1 ? part : nullptr;
+    const int slots = bwd_var_slots(L, ksplit);
+    ra::TileShares ts;
+    ts.var = 0;
+    if (slots) {
+      const std::vector<long long> w = single_walks(L, d->cp_size, d->rank);
+      rkq.q_tiles = plan_tile_parts(w, (long long)ksplit * (long long)w.size(), slots, &rkq, ts.n);
+      ts.var = 1;
+    }
+    a.ksplit = slots ? slots : ksplit;
+    a.dq_part = a.ksplit > 1 ? part : nullptr;
     if (d->events && d->events[0] &&
         (e = hipEventRecord((hipEvent_t)d->events[0], hs)) != hipSuccess)
       return hip_fail(e, "event record");
@@ -1260,7 +1298,7 @@ ra_status ra_rank_backward(const ra_rank_bwd_desc* d, void* stream) {
                              delta, hs);
     if (e != hipSuccess) return hip_fail(e, "delta launch");
     if (a.n_qtiles > 0) {
-      e = ra::launch_rank_bwd_bf16(a, rk, rkq, rg, L.dqk, L.dv, hs);
+      e = ra::launch_rank_bwd_bf16(a, rk, rkq, rg, ts, L.dqk, L.dv, hs);
       if (e == hipErrorInvalidValue) return fail(RA_ERR_UNSUPPORTED, "backward variant not built");
       if (e != hipSuccess) return hip_fail(e, "rank backward launch");
     }

@@ -621,15 +621,31 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a, RankKV r
   // per XCD.  A rank share: the kv head is the slowest index, so an XCD's
   // contiguous range is one kv head's query tiles over all documents, which
   // all walk that head's K/V tiles of every block (kept in the XCD's L2).
-  const int nks = max(a.ksplit, 1);  // workgroups sharing a query tile
-  int b = (!RANK && a.n_seq > 1) ? xcd_deal(blockIdx.x, gridDim.x, a.group * nks)
-                                 : xcd_remap(blockIdx.x, gridDim.x);
-  const int kshare = b % nks;  // this workgroup takes tiles kshare, kshare + nks, ... of the walk
-  b /= nks;
+  // Per-tile key shares of a single sequence (rk.var_split): units of
+  // (query tile, share, shares), heaviest first, the kv heads of a unit
+  // next to each other and dealt over the XCDs (an XCD then keeps to one kv
+  // head's K/V when there are 8).
+  const bool var = RANK && rk.var_split;
+  int nks = max(a.ksplit, 1);  // workgroups sharing a query tile
+  int b = ((!RANK && a.n_seq > 1) || var)
+              ? xcd_deal(blockIdx.x, gridDim.x, var ? a.group : a.group * nks)
+              : xcd_remap(blockIdx.x, gridDim.x);
+  int kshare = 0;  // this workgroup takes tiles kshare, kshare + nks, ... of the walk
+  if (!var) {
+    kshare = b % nks;
+    b /= nks;
+  }
   const int hg = b % a.group;
   b /= a.group;
   int kvh, seg, qt;
-  if (RANK) {
+  if (var) {
+    kvh = b % a.hkv;
+    const int e = rk.tile_order[b / a.hkv];
+    seg = 0;
+    qt = e >> 6;
+    kshare = (e >> 3) & 7;
+    nks = (e & 7) + 1;
+  } else if (RANK) {
     // only live tiles: per kv head, each segment's query tiles, the
     // heaviest (last rows) first; packed segments in the host's
     // heaviest-first order of those tiles
@@ -952,7 +968,8 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(AttnArgs a, RankKV r
 // for every row the dQ launch covered (rows inside the q part of a segment
 // whose k part is not empty).  One thread per 4 floats of a row's
 // [hq, dqk] gradient; HBM-bound.
-__global__ __launch_bounds__(256) void bwd_ksplit_reduce_kernel(AttnArgs a, int dqk) {
+__global__ __launch_bounds__(256) void bwd_ksplit_reduce_kernel(AttnArgs a, int dqk,
+                                                                 TileShares ts) {
   const int row4 = a.hq * dqk / 4;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)a.total_q * row4) return;
@@ -969,7 +986,9 @@ __global__ __launch_bounds__(256) void bwd_ksplit_reduce_kernel(AttnArgs a, int 
   const int64_t off = (int64_t)row * a.hq * dqk + 4 * c;
   const int64_t stride = (int64_t)a.total_q * a.hq * dqk;
   float4 acc = *reinterpret_cast<const float4*>(a.dq + off);
-  for (int s = 1; s < a.ksplit; ++s) {
+  // per-tile shares: this row's 128-row tile has ts.n[tile] of them
+  const int ns = ts.var ? ts.n[(row - q_lo) >> 7] : a.ksplit;
+  for (int s = 1; s < ns; ++s) {
     const float4 x = *reinterpret_cast<const float4*>(a.dq_part + (s - 1) * stride + off);
     acc.x += x.x;
     acc.y += x.y;
@@ -1027,7 +1046,11 @@ hipError_t launch_attn_bwd_bf16(const AttnArgs& a0, int dqk, int dv, bool causal
     const long long nb = (n4 + 255) / 256;
     if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (nb > 0)
-      hipLaunchKernelGGL(bwd_ksplit_reduce_kernel, dim3((unsigned)nb), dim3(256), 0, st, a, dqk);
+      {
+      TileShares ts;
+      ts.var = 0;
+      hipLaunchKernelGGL(bwd_ksplit_reduce_kernel, dim3((unsigned)nb), dim3(256), 0, st, a, dqk, ts);
+    }
   }
   if (ak.qsplit > 1 && nk > 0) {
     const long long n4 = (long long)total_k * a.hkv * (dqk + dv) / 4;
@@ -1041,7 +1064,8 @@ hipError_t launch_attn_bwd_bf16(const AttnArgs& a0, int dqk, int dv, bool causal
 }
 
 hipError_t launch_rank_bwd_bf16(const AttnArgs& a0, const RankKV& rk, const RankKV& rkq,
-                                const RankGrad& rg, int dqk, int dv, hipStream_t st) {
+                                const RankGrad& rg, const TileShares& ts, int dqk, int dv,
+                                hipStream_t st) {
   // the dQ grid is kv heads x rk.q_tiles live 128-row query tiles x group x
   // key shares, the dK/dV grid kv heads x rk.kv_tile_off[rk.cp] live
   // 128-key tiles
@@ -1050,7 +1074,8 @@ hipError_t launch_rank_bwd_bf16(const AttnArgs& a0, const RankKV& rk, const Rank
   a.k_part = RA_PART_ALL;
   a.qsplit = 1;
   if (a.ksplit < 1 || !a.dq_part) a.ksplit = 1;
-  const long long nq = (long long)a.hkv * rkq.q_tiles * a.group * a.ksplit;
+  // per-tile shares: rkq.q_tiles counts (tile, share) units
+  const long long nq = (long long)a.hkv * rkq.q_tiles * a.group * (rkq.var_split ? 1 : a.ksplit);
   const long long nk = (long long)a.hkv * rk.kv_tile_off[rk.cp];
   if (nq > 0x7fffffffLL || nk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (dqk == 128 && dv == 128) {
@@ -1075,7 +1100,7 @@ hipError_t launch_rank_bwd_bf16(const AttnArgs& a0, const RankKV& rk, const Rank
     const long long nb = (n4 + 255) / 256;
     if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (nb > 0)
-      hipLaunchKernelGGL(bwd_ksplit_reduce_kernel, dim3((unsigned)nb), dim3(256), 0, st, a, dqk);
+      hipLaunchKernelGGL(bwd_ksplit_reduce_kernel, dim3((unsigned)nb), dim3(256), 0, st, a, dqk, ts);
   }
   return hipGetLastError();
 }

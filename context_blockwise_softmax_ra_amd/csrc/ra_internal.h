@@ -197,8 +197,16 @@ hipError_t launch_attn_bwd_bf16(const AttnArgs& a, int dqk, int dv, bool causal,
 // over a.ksplit workgroups, partials reduced in share order).  a describes
 // the rank's local rows (q, dout, lse, delta, dq; parts ALL); rk the
 // owners' K/V blocks.
+// Key shares per 128-row query tile of a single-sequence rank-fused dQ
+// launch (var = 1): the reduction adds shares 1 .. n[tile] - 1.
+struct TileShares {
+  int32_t var;
+  uint8_t n[kMaxTileOrder];
+};
+
 hipError_t launch_rank_bwd_bf16(const AttnArgs& a, const RankKV& rk_kv, const RankKV& rk_q,
-                                const RankGrad& rg, int dqk, int dv, hipStream_t st);
+                                const RankGrad& rg, const TileShares& ts, int dqk, int dv,
+                                hipStream_t st);
 
 // Sets the thread-local message ra_last_error() returns and passes st back.
 ra_status set_error(ra_status st, const char* fmt, ...);

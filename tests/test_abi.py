@@ -291,16 +291,24 @@ def test_rank_backward_workspace_sizes(qsplit_env, n_parts, monkeypatch):
     assert sizes == {hq * T * 4 + n_parts * T * hkv * (128 + 128) * 4}
 
 
-@pytest.mark.parametrize("T,hq,hkv,C,ksplit_env,n_parts", [
-    (4096, 32, 8, 8, None, 0),    # 32K GQA rank: 1024 dQ workgroups, no split
-    (2048, 8, 8, 4, None, 1),     # 8K MHA rank: 128 dQ workgroups, split in 2
-    (2048, 8, 8, 4, "4", 3),
+@pytest.mark.parametrize("T,hq,hkv,C,ksplit_env,var,n_parts", [
+    (4096, 32, 8, 8, None, None, 0),  # 32K GQA rank: 1024 dQ workgroups, no split
+    (2048, 8, 8, 4, None, None, 5),   # 8K MHA rank: 128 dQ workgroups, split in 2, per tile: 6 slots
+    (2048, 8, 8, 4, None, "0", 1),    # the same with uniform shares: 2
+    (2048, 8, 8, 4, "4", "0", 3),
+    (2048, 8, 8, 4, "8", "0", 3),     # at most 4 shares
 ])
-def test_rank_fused_backward_workspace_sizes(T, hq, hkv, C, ksplit_env, n_parts, monkeypatch):
+def test_rank_fused_backward_workspace_sizes(T, hq, hkv, C, ksplit_env, var, n_parts,
+                                             monkeypatch):
     """Rank-fused backward: delta [hq, T] plus the float32 dQ partials
-    [T, hq, dqk] of key shares 1 .. ksplit-1, the same for every rank; the
-    dK/dV launch over all owners needs no partials."""
+    [T, hq, dqk] of key shares 1 .. ksplit-1 (share slots 1 .. 5 when a
+    single sequence's shares are dealt per tile), the same for every rank;
+    the dK/dV launch over all owners needs no partials."""
     monkeypatch.setenv("RA_BWD_RANK_FUSED", "1")
+    if var is None:
+        monkeypatch.delenv("RA_BWD_VAR_SPLIT", raising=False)
+    else:
+        monkeypatch.setenv("RA_BWD_VAR_SPLIT", var)
     if ksplit_env is None:
         monkeypatch.delenv("RA_BWD_KSPLIT", raising=False)
     else:

@@ -205,13 +205,17 @@ def test_mla_backward_reduced_full_parity():
 # RA_BWD_KV_SPLIT, RA_BWD_KSPLIT); "auto" leaves the choice to the library
 # (rank-fused).  Rank-fused ("1"): one dK/dV
 # launch over every owner's key tiles and one dQ launch walking all blocks,
-# ksplit = workgroups sharing a dQ query tile.  Per step ("0"): one pair of
+# ksplit = workgroups sharing a dQ query tile (on a single sequence dealt
+# over the tiles by walk length, up to 6 per tile, unless "_uniform").
+# Per step ("0"): one pair of
 # launches per ring step; qsplit = workgroups sharing a dK/dV key tile,
 # ksplit = workgroups sharing a dQ query tile (partials in the workspace,
 # added in share order); the query split over a workgroup's waves
 # (KV_SPLIT=1) only runs where qsplit is 1.
 BWD_SPLITS = {
     "auto": (None, None, None, None),
+    "fused_ksplit2_uniform": ("1", None, None, "2", "0"),
+    "fused_ksplit4_uniform": ("1", None, None, "4", "0"),
     "fused_ksplit1": ("1", None, None, "1"),
     "fused_ksplit2": ("1", None, None, "2"),
     "fused_ksplit3": ("1", None, None, "3"),
@@ -230,9 +234,10 @@ BWD_SPLITS = {
 
 
 def _set_splits(monkeypatch, mode):
-    fused, qs, kv, ks = BWD_SPLITS[mode]
+    fused, qs, kv, ks, var = (BWD_SPLITS[mode] + (None,))[:5]
     for name, val in (("RA_BWD_RANK_FUSED", fused), ("RA_BWD_QSPLIT", qs),
-                      ("RA_BWD_KV_SPLIT", kv), ("RA_BWD_KSPLIT", ks)):
+                      ("RA_BWD_KV_SPLIT", kv), ("RA_BWD_KSPLIT", ks),
+                      ("RA_BWD_VAR_SPLIT", var)):
         if val is None:
             monkeypatch.delenv(name, raising=False)
         else:
