@@ -287,8 +287,10 @@ ra_status ra_block_attn_bwd(const ra_attn_desc* d, const void* dout, const float
  * owner's block (each with that step's rule, added into that owner's
  * dK/dV) and one dQ launch whose query tiles walk the key tiles of all
  * blocks in ring order, dQ kept in registers; on shares with few query
- * tiles up to 4 workgroups deal a query tile's walk, their float32 partials
- * (after delta in the workspace) added in share order.
+ * tiles up to 4 workgroups deal a query tile's walk (on a single sequence
+ * the same number of workgroups is dealt over the tiles by walk length, up
+ * to 6 per tile; RA_BWD_VAR_SPLIT=0 keeps them uniform), their float32
+ * partials (after delta in the workspace) added in share order.
  *
  * RA_BWD_RANK_FUSED=0 in the environment selects the per-step form
  * instead: one dK/dV and one dQ launch per ring step.  On blocks with few
