@@ -11,6 +11,9 @@
   the last 256 keys in full, and the sum rules over every key.
 * The 16K copy of the 256K MLA workload (S=16384, CP=32: 256-token chunks,
   16 heads, d_qk 192, d_v 128): every rank's forward and backward in full.
+* The 128K packed mix (23 documents, CP=16) backward at full size: every
+  gradient element of its nine shortest documents, sampled dQ rows of the
+  three longest, and the sum rule of dV per document.
 
 The comparison follows the pages' own check of a context-parallel
 implementation: run the complete sequence and compare the complete outputs
@@ -194,3 +197,55 @@ def test_mla_16k_cp32_forward_full_parity(monkeypatch):
 @pytest.mark.parametrize("fused", [True, False], ids=["rank_fused", "per_step"])
 def test_mla_16k_cp32_backward_full_parity(fused, monkeypatch):
     _full_backward(_mla_mini(), monkeypatch, fused)
+
+
+def test_varlen_128k_backward_full_size(monkeypatch):
+    """The 128K packed mix (23 documents, CP = 16) backward at full size on
+    the default path: every dQ, dK, dV element of the nine documents of at
+    most 2048 tokens against the oracle's gradients of each document; dQ of
+    sampled rows (both chunk ends and random) of the three longest
+    documents; and the sum rule of dV over every document (the probabilities
+    of a row sum to 1, so the dV of a document's keys sums to its dO).
+    Rows of the short documents attend to few keys and reach |dQ| = 6.6 at
+    the workload's dO scale, so dO is scaled by 2^-2 (exact in bf16; every
+    gradient and its rounding error scale alike) to apply the fixed bars at
+    unit magnitude."""
+    for v in ("RA_BWD_RANK_FUSED", "RA_BWD_QSPLIT", "RA_BWD_KSPLIT", "RA_BWD_KV_SPLIT",
+              "RA_BWD_VAR_SPLIT"):
+        monkeypatch.delenv(v, raising=False)
+    w = synth.WORKLOADS["varlen_128k"]
+    log(f"varlen_128k backward (full size): S={w.seqlen} C={w.cp}")
+    prob, (q, k, v, do) = make_problem(w, with_dout=True, dout_scale=0.25)
+    q64, k64, v64, do64 = to_np(q), to_np(k), to_np(v), to_np(do)
+    _, _, dqs, dks, dvs = _backward_all(prob)
+    gq, gk, gv = _concat_grads(prob, dqs, dks, dvs)
+    cu = w.cu_global()
+    lens = np.diff(cu)
+    for d in np.argsort(lens):
+        a, b = int(cu[d]), int(cu[d + 1])
+        if b - a > 2048:
+            break
+        rq, rk, rv = oracle_grads(q64[a:b], k64[a:b], v64[a:b], do64[a:b],
+                                  np.array([0, b - a], np.int32))
+        check_out(gq[a:b], rq, "bf16", f"doc {d} ({b - a} tokens) dQ")
+        check_out(gk[a:b], rk, "bf16", f"doc {d} dK")
+        check_out(gv[a:b], rv, "bf16", f"doc {d} dV")
+    lay = oracle.ref.Layout(cu)
+    rng = np.random.default_rng(7)
+    for d in np.argsort(lens)[-3:]:
+        a, b = int(cu[d]), int(cu[d + 1])
+        c = (b - a) // (2 * w.cp)
+        ends = [a, a + c - 1, a + c, b - c - 1, b - c, b - 1]
+        rows = np.unique(np.concatenate([ends, rng.integers(a, b, 4)]))
+        ref = np.zeros((len(rows), w.hq, w.dqk))
+        for i, r in enumerate(rows):
+            s = slice(a, int(r) + 1)  # the row's visible keys: its document up to itself
+            ref[i] = oracle.attention_bwd(q64[r:r + 1], k64[s], v64[s], do64[r:r + 1],
+                                          lay.pos[r:r + 1], lay.doc[r:r + 1], lay.pos[s],
+                                          lay.doc[s])[0][0]
+        check_out(gq[rows], ref, "bf16", f"doc {d} ({b - a} tokens) sampled dQ rows")
+    for d in range(len(lens)):
+        a, b = int(cu[d]), int(cu[d + 1])
+        sdv, sdo = gv[a:b].sum(0), do64[a:b].sum(0)
+        rel = np.abs(sdv - sdo).max() / np.abs(sdo).max()
+        assert rel <= 1e-3, (d, rel)
