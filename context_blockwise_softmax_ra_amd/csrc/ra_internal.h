@@ -75,9 +75,10 @@ struct RankKV {
   const void* k[kMaxCp];
   const void* v[kMaxCp];
   int32_t cp, rank;
-  // KV split of a rank share (4-wave kernel): part p of `split` walks the
-  // blocks p, p + split, ... and writes its float32 partial (out, lse) at
-  // out + p * part_out_stride, lse + p * part_lse_stride (elements)
+  // KV split of a rank share (4-wave kernel): part p of `split` takes the
+  // key tiles p, p + split, ... of the share's walk (all blocks in ring
+  // order) and writes its float32 partial (out, lse) at out + p *
+  // part_out_stride, lse + p * part_lse_stride (elements)
   int32_t split;
   int64_t part_out_stride, part_lse_stride;
   // rank-fused dK/dV launch: kv_tile_off[o] counts the 128-key tiles (with
@@ -101,10 +102,13 @@ struct RankKV {
   // more tiles than the order holds); 0: unit u takes tile u
   int32_t fwd_tiles;
   int32_t tile_ordered;
-  // KV split with per-tile parts (4-wave kernel, single sequence): unit u
-  // of fwd_tiles per head is tile_order[u] = query tile << 6 | part << 3 |
-  // parts - 1; split is then the number of partial slots, and part 0 of a
-  // tile sets lse = -inf in the slots past its tile's parts
+  // Per-tile parts of a single sequence, tile_order[u] = query tile << 6 |
+  // part << 3 | parts - 1 for unit u, heaviest part first:
+  //  - forward KV split (4-wave kernel): fwd_tiles units per head; split is
+  //    then the number of partial slots, and part 0 of a tile sets
+  //    lse = -inf in the slots past its tile's parts;
+  //  - rank-fused dQ key shares: q_tiles units per head; the share
+  //    reduction takes each tile's count from TileShares.
   int32_t var_split;
   uint16_t tile_order[kMaxTileOrder];
 };
