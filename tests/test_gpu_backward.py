@@ -300,6 +300,25 @@ def _per_document_reference(q64, k64, v64, do64, cu):
     return ro, rl, rq, rk, rv
 
 
+SMALL_BWD_SHARES = [(520, 2, 2), (1000, 1, 2), (392, 4, 1), (2056, 2, 4)]
+
+
+@pytest.mark.parametrize("var", ["0", "1"], ids=["uniform", "per_tile"])
+@pytest.mark.parametrize("ksplit", [None, "4"], ids=["auto", "ksplit4"])
+@pytest.mark.parametrize("shape", SMALL_BWD_SHARES,
+                         ids=[f"S{s}_C{c}_h{h}" for s, c, h in SMALL_BWD_SHARES])
+def test_small_share_dq_shares(shape, ksplit, var, monkeypatch):
+    """Small single-sequence shares in the rank-fused backward with dQ key
+    shares, uniform and dealt per tile (tiles whose walk is shorter than
+    their shares, tiles with a single share): every gradient element."""
+    S, C, H = shape
+    _set_splits(monkeypatch, "auto")
+    monkeypatch.setenv("RA_BWD_VAR_SPLIT", var)
+    if ksplit is not None:
+        monkeypatch.setenv("RA_BWD_KSPLIT", ksplit)
+    _full_bwd_parity(synth.reduced("mha_8k", S, C, hq=H, hkv=H))
+
+
 # Packed streams whose tile lists take each ordering of the rank-fused
 # grids: heaviest-first by tile (up to 512 tiles), by segment (more tiles,
 # at most 512 segments) and the plain list order (more segments).

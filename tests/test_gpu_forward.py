@@ -426,6 +426,34 @@ def test_fused_rank_share_kv_split(split, out_dtype, var, monkeypatch):
         check_lse(lses[r], rl[:, rows], f"rank{r} split {split}")
 
 
+SMALL_SHARES = [(520, 2, 2), (1000, 1, 2), (392, 4, 1), (2056, 2, 4)]
+
+
+@pytest.mark.parametrize("var", ["0", "1"], ids=["uniform", "per_tile"])
+@pytest.mark.parametrize("split", [None, "8"], ids=["auto", "split8"])
+@pytest.mark.parametrize("shape", SMALL_SHARES, ids=[f"S{s}_C{c}_h{h}" for s, c, h in SMALL_SHARES])
+def test_small_share_kv_split_shapes(shape, split, var, monkeypatch):
+    """Small single-sequence shares (a few ragged 128-row tiles, one to
+    four ranks, 1-4 heads) on the fused path with the KV split: every rank's
+    output and lse against the oracle, with uniform and per-tile parts
+    (tiles whose walk is shorter than their parts, unused partial slots)."""
+    S, C, H = shape
+    monkeypatch.setenv("RA_FWD_VAR_SPLIT", var)
+    monkeypatch.delenv("RA_FWD_KERNEL", raising=False)
+    if split is None:
+        monkeypatch.delenv("RA_FWD_KV_SPLIT", raising=False)
+    else:
+        monkeypatch.setenv("RA_FWD_KV_SPLIT", split)
+    w = synth.reduced("mha_8k", S, C, hq=H, hkv=H)
+    prob, (q, k, v, _) = make_problem(w)
+    ro, rl = oracle.full_attention(to_np(q), to_np(k), to_np(v), w.cu_global())
+    outs, lses = _run_all_ranks(prob, torch.bfloat16, 2)
+    for r in range(C):
+        rows = prob.rows(r)
+        check_out(outs[r], ro[rows], "bf16", f"rank{r}")
+        check_lse(lses[r], rl[:, rows], f"rank{r}")
+
+
 def test_mha_8k_workload_full_parity():
     _full_parity(synth.WORKLOADS["mha_8k"], determinism=True)
 
