@@ -313,6 +313,31 @@ def blas_vendor() -> str:
     return "unknown"
 
 
+def _timed_steps(run_step, ev, a, torch, stream):
+    """Warm-up, then a.steps timed steps with no per-launch events (an event
+    recorded between two launches leaves a gap of ~10 us before the next),
+    then the same number of steps recording ev[i] for the per-launch times.
+    Returns the timed steps' ms per step."""
+    for e3 in ev:  # recorded once before the timed region
+        for e2 in e3:
+            for e in e2:
+                e.record(stream)
+    for _ in range(a.warmup):
+        run_step()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(a.steps):
+        run_step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / a.steps
+    for i in range(a.steps):
+        run_step(ev[i])
+    torch.cuda.synchronize()
+    return ms_step
+
+
 def bench_backward(a, w, prob, torch, L):
     """Backward step: every rank's ra_rank_backward (delta, then dK/dV over
     every owner's key tiles and dQ over all blocks in one launch each, or
@@ -350,23 +375,9 @@ def bench_backward(a, w, prob, torch, L):
             prob.backward(r, fwd[r][0], fwd[r][1], dqs[r], dks, dvs, ws,
                           events=None if events is None else events[r])
 
-    for _ in range(a.warmup):
-        run_step()
-    torch.cuda.synchronize()
     ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2 * C)] for _ in range(C)]
           for _ in range(a.steps)]
-    for e3 in ev:
-        for e2 in e3:
-            for e in e2:
-                e.record(stream)
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(a.steps):
-        run_step(ev[i])
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / a.steps
+    ms_step = _timed_steps(run_step, ev, a, torch, stream)
     # both forms record event 0 before a rank's first launch and event 2C-1
     # after its last: the rank's span
     blk_ms = sum(ev[i][r][0].elapsed_time(ev[i][r][2 * C - 1])
@@ -408,23 +419,9 @@ def bench_ulysses(a, w, q, k, v, torch, L):
         for r in range(C):
             uly.forward(r, *bufs[r], events=None if events is None else events[r])
 
-    for _ in range(a.warmup):
-        run_step()
-    torch.cuda.synchronize()
     ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(C)]
           for _ in range(a.steps)]
-    for e3 in ev:
-        for e2 in e3:
-            for e in e2:
-                e.record(stream)
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(a.steps):
-        run_step(ev[i])
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / a.steps
+    ms_step = _timed_steps(run_step, ev, a, torch, stream)
     per_rank_ms = [sum(ev[i][r][0].elapsed_time(ev[i][r][1]) for i in range(a.steps)) / a.steps
                    for r in range(C)]
     achieved = step_flops / (sum(per_rank_ms) / 1e3) / 1e12
@@ -468,23 +465,9 @@ def bench_map(a, w, q, k, v, torch, L):
         for r in range(C):
             prob.forward(r, *bufs[r], events=None if events is None else events[r])
 
-    for _ in range(a.warmup):
-        run_step()
-    torch.cuda.synchronize()
     ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2 * C)] for _ in range(C)]
           for _ in range(a.steps)]
-    for e3 in ev:
-        for e2 in e3:
-            for e in e2:
-                e.record(stream)
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(a.steps):
-        run_step(ev[i])
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / a.steps
+    ms_step = _timed_steps(run_step, ev, a, torch, stream)
     rank_ms = [sum(ev[i][r][2 * s].elapsed_time(ev[i][r][2 * s + 1])
                    for i in range(a.steps) for s in range(C)) / a.steps for r in range(C)]
     achieved = step_flops / (sum(rank_ms) / 1e3) / 1e12
