@@ -29,8 +29,10 @@
  *     contiguous; lse and delta are [heads, tokens] float32.
  *   - Packed sequences: segment s covers tokens [cu[s], cu[s+1]) of a
  *     buffer.  Both a host and a device copy of every cu_seqlens array are
- *     passed: the host copy is used for validation and launch sizing only
- *     (it is not retained), the device copy by the kernels.
+ *     passed and must hold the same values: the host copy is used for
+ *     validation, launch sizing and the order of a launch's tiles (it is
+ *     not retained), the device copy by the kernels, which locate their
+ *     tiles in it.
  *   - Ownership: the caller allocates and frees every buffer, including
  *     workspaces; the library keeps no pointer after a call returns, keeps
  *     no state except a thread-local error string, never synchronises and
