@@ -70,7 +70,7 @@ def parse():
     ap.add_argument("--bwd-rank-fused", type=int, default=-1,
                     help="backward: 1 = one dK/dV and one dQ launch per rank share (every owner's "
                          "blocks), 0 = one pair of launches per ring step, -1 = the library's "
-                         "choice (fused for packed documents and small shares)")
+                         "choice (rank-fused)")
     ap.add_argument("--merge", type=int, default=0,
                     help="1: time ra_lse_merge alone on the workload's full-row step (every "
                          "local row, every query head, fp32 partials) and report HBM GB/s")
