@@ -255,6 +255,46 @@ __global__ __launch_bounds__(NT) void bwd_delta_kernel(const void* __restrict__ 
   }
 }
 
+// The same for bf16 out and dout with d_v a multiple of 8 and 16-byte aligned
+// rows: each lane of a row's 16-lane group takes 8 consecutive elements per
+// pass with one 16-byte load from each buffer (the form above issues one
+// 2-byte load per element).
+__device__ __forceinline__ float dot_bf16x8(const uint4& a, const uint4& b) {
+  const uint32_t x[4] = {a.x, a.y, a.z, a.w}, y[4] = {b.x, b.y, b.z, b.w};
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc = fmaf(__uint_as_float(x[i] << 16), __uint_as_float(y[i] << 16), acc);
+    acc = fmaf(__uint_as_float(x[i] & 0xffff0000u), __uint_as_float(y[i] & 0xffff0000u), acc);
+  }
+  return acc;
+}
+
+__global__ __launch_bounds__(NT) void bwd_delta_bf16x8_kernel(const uint4* __restrict__ out,
+                                                              const uint4* __restrict__ dout,
+                                                              int total_t, int h, int dv8,
+                                                              float* __restrict__ delta) {
+  const int lane = threadIdx.x & 63;
+  const int sub = lane >> 4, li = lane & 15;
+  const int64_t nrows = (int64_t)total_t * h;
+  const int64_t wave_global = (int64_t)blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
+  const int64_t wstride = (int64_t)gridDim.x * (NT / 64);
+  for (int64_t base = wave_global * 4; base < nrows; base += wstride * 4) {
+    const int64_t rh = base + sub;
+    float acc = 0.f;
+    if (rh < nrows) {
+      const int64_t off = rh * dv8;
+      for (int d = li; d < dv8; d += 16) acc += dot_bf16x8(out[off + d], dout[off + d]);
+    }
+#pragma unroll
+    for (int s = 8; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 16);
+    if (rh < nrows && li == 0) {
+      const int64_t t = rh / h, hh = rh % h;
+      delta[hh * total_t + t] = acc;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Combine of a KV-split rank share: the same lse weighting as the merge
 // above, over `split` partials at once (weights exp(lse_p - max), summed in
@@ -472,6 +512,13 @@ hipError_t launch_bwd_delta(const void* out, int out_dtype, const void* dout, in
                             hipStream_t st) {
   const int64_t rows = (int64_t)total_t * hq;
   if (rows <= 0) return hipSuccess;
+  if (out_dtype == RA_BF16 && dout_dtype == RA_BF16 && dv % 8 == 0 &&
+      reinterpret_cast<uintptr_t>(out) % 16 == 0 && reinterpret_cast<uintptr_t>(dout) % 16 == 0) {
+    hipLaunchKernelGGL(bwd_delta_bf16x8_kernel, dim3(grid_for(rows, 16, 16384u)), dim3(NT), 0, st,
+                       static_cast<const uint4*>(out), static_cast<const uint4*>(dout), total_t,
+                       hq, dv / 8, delta);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(bwd_delta_kernel, dim3(grid_for(rows, 16, 16384u)), dim3(NT), 0, st, out,
                      out_dtype, dout, dout_dtype, total_t, hq, dv, delta);
   return hipGetLastError();

@@ -197,6 +197,28 @@ def _full_bwd_parity(w, dout_scale=1.0):
     check_out(gv, rv, "bf16", "dV")
 
 
+@pytest.mark.parametrize("odt,ddt", [(torch.bfloat16, torch.bfloat16),
+                                     (torch.float32, torch.bfloat16),
+                                     (torch.bfloat16, torch.float32)])
+@pytest.mark.parametrize("T,H,dv", [(1000, 3, 128), (77, 5, 64), (33, 2, 192), (5, 1, 8),
+                                    (7, 3, 12)])
+def test_attn_bwd_delta_parity(T, H, dv, odt, ddt):
+    """delta[h, t] = dO[t, h, :] . O[t, h, :] against the oracle's definition,
+    on bf16 and float32 inputs (the bf16 pair with d_v a multiple of 8 takes
+    16-byte loads, the others the per-element form), ragged sizes."""
+    g = torch.Generator().manual_seed(T * 31 + dv)
+    out = torch.randn(T, H, dv, generator=g).to(odt)
+    do = torch.randn(T, H, dv, generator=g).to(ddt)
+    delta = torch.full((H, T), float("nan"), device=DEV)
+    L.ra_attn_bwd_delta(out.to(DEV), do.to(DEV), delta)
+    torch.cuda.synchronize()
+    ref = oracle.bwd_delta(to_np(out), to_np(do))
+    scale = np.einsum("thd,thd->ht", np.abs(to_np(do)), np.abs(to_np(out)))
+    err = np.abs(to_np(delta) - ref)
+    assert not np.isnan(to_np(delta)).any()
+    assert (err <= 1e-5 * scale + 1e-30).all(), err.max()
+
+
 def test_mla_backward_reduced_full_parity():
     _full_bwd_parity(synth.reduced("mla_256k", 4096, 8))
 
