@@ -157,6 +157,20 @@ def oracle_rows(q64, k64, v64, cu, rows):
             np.concatenate([l for _, l in res], axis=0))
 
 
+def oracle_attention_by_document(q64, k64, v64, cu):
+    """oracle.attention of every row of a packed stream, one document at a
+    time: documents see only their own keys, so this equals the oracle's
+    whole-stream call (full_attention) at a fraction of its cost."""
+    lay = oracle.ref.Layout(cu)
+    ro = np.zeros(q64.shape[:2] + (v64.shape[2],))
+    rl = np.zeros((q64.shape[1], q64.shape[0]))
+    for d in range(len(cu) - 1):
+        s = slice(int(cu[d]), int(cu[d + 1]))
+        ro[s], rl[:, s] = oracle.attention(q64[s], k64[s], v64[s], lay.pos[s], lay.doc[s],
+                                           lay.pos[s], lay.doc[s])
+    return ro, rl
+
+
 def oracle_grads(q64, k64, v64, do64, cu):
     """oracle.attention_bwd of the whole stream (every row over every key),
     one query head at a time; query heads of a group add their dK, dV."""

@@ -17,7 +17,7 @@ import torch
 import oracle
 import synth
 from gpu_util import (check_lse, check_out, global_inputs, log, make_problem, metrics,
-                      sample_rows, to_np)
+                      oracle_attention_by_document, sample_rows, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -385,7 +385,7 @@ def _full_parity(w, fuse_modes=(0, 1, 2), determinism=False):
     log(f"workload {w.name}: S={w.seqlen} C={w.cp} hq={w.hq} hkv={w.hkv} d={w.dqk}/{w.dv}")
     prob, (q, k, v, _) = make_problem(w)
     q64, k64, v64 = to_np(q), to_np(k), to_np(v)
-    ro, rl = oracle.full_attention(q64, k64, v64, w.cu_global())
+    ro, rl = oracle_attention_by_document(q64, k64, v64, w.cu_global())
     for kernel in KERNELS:
         for fuse in fuse_modes:
             tag = f"fuse={fuse} kernel={kernel}"

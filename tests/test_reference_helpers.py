@@ -1,16 +1,17 @@
 """CPU check of the full-size reference helpers of the GPU tests.
 
 ``gpu_util.oracle_rows`` and ``gpu_util.oracle_grads`` call the oracle once
-per query head (and, for rows, with each run's visible key prefix only) so
-that whole full-size rank shares can be compared in seconds.  They must
-give exactly what one plain call of the oracle gives: packed documents,
-grouped heads, rows in several runs per document.
+per query head (and, for rows, with each run's visible key prefix only),
+and ``gpu_util.oracle_attention_by_document`` once per document, so that
+whole full-size rank shares can be compared in seconds.  They must give
+exactly what one plain call of the oracle gives: packed documents, grouped
+heads, rows in several runs per document.
 """
 import numpy as np
 
 import oracle
 import synth
-from gpu_util import oracle_grads, oracle_rows
+from gpu_util import oracle_attention_by_document, oracle_grads, oracle_rows
 
 
 def _inputs(lengths, hq, hkv, dqk, dv, seed):
@@ -46,3 +47,11 @@ def test_oracle_grads_equals_plain_oracle():
     got = oracle_grads(q, k, v, do, cu)
     for a, b in zip(got, ref):
         assert np.allclose(a, b, rtol=0, atol=1e-12)
+
+
+def test_oracle_by_document_equals_plain_oracle():
+    cu, q, k, v, _ = _inputs([40, 1, 96, 63, 2], 6, 2, 16, 8, 3)
+    got_o, got_l = oracle_attention_by_document(q, k, v, cu)
+    ref_o, ref_l = oracle.full_attention(q, k, v, cu)
+    assert np.allclose(got_o, ref_o, rtol=0, atol=1e-13)
+    assert np.allclose(got_l, ref_l, rtol=0, atol=1e-13)
